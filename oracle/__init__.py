@@ -1,0 +1,28 @@
+"""fp64 CPU oracle for the exact attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this package:
+only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may call it.  It shares no code with the HIP library.
+
+Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
+
+  attention / attention_rows   pinned: worked two-score example of the page,
+                               closed forms (two keys, uniform scores, causal
+                               row 0, hard attention), scipy softmax and
+                               logsumexp, mpmath brute force, LSE merge,
+                               permutation equivariance, varlen = per-document
+  online_softmax_states        pinned: the page's worked example states, in
+                               both orders, and agreement with attention()
+  e4m3_decode                  pinned: OCP e4m3fn closed-form values and torch's
+                               float8_e4m3fn decode of all 256 bytes
+  bf16_decode                  pinned: torch's bfloat16 decode of all 65536
+                               bit patterns
+  dequantize_e4m3_blocks       pinned: exact round trip with scale 1 blocks and
+                               hand-built blocks
+"""
+from .exact import (attention, attention_rows, online_softmax_states,
+                        e4m3_decode, bf16_decode, dequantize_e4m3_blocks,
+                        visible_keys)
+
+__all__ = ["attention", "attention_rows", "online_softmax_states",
+           "e4m3_decode", "bf16_decode", "dequantize_e4m3_blocks", "visible_keys"]
