@@ -1,0 +1,238 @@
+"""Throughput of the exact attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+A step is one attention forward (one kernel launch) over the whole workload,
+inputs already resident in device memory.  Throughput is attention TFLOP/s
+with the dense convention 4 * B * H * N^2 * d, halved for causal masking
+(packed documents: sum over documents of 2 * H * L^2 * d); the
+FlashAttention pages count the work this way because every query-key pair
+is still processed ("Flash Attention và IO", section "Tiling giữ công việc ở
+gần nơi tính").
+
+Prints ONE JSON line with the metric, the roofline of the kernel (its
+average launch time measured with HIP events on the launch stream) and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of MFMA peak (bf16 causal, B·H·N²·d)"
+PEAK = {"bf16": 2516.6, "fp8": 5033.2}     # dense MFMA TFLOP/s, 256 CU x 2.4 GHz
+HBM_PEAK = 8000.0                            # GB/s
+
+
+def flops(w, lengths=None):
+    if w.varlen:
+        return float(sum(2 * w.H * int(L) ** 2 * w.d for L in lengths))
+    f = 4.0 * w.B * w.H * w.N ** 2 * w.d
+    return f / 2 if w.causal else f
+
+
+def algorithmic_bytes(w):
+    """Q, K, V read once plus O and LSE written once."""
+    tokens = w.N if w.varlen else w.B * w.N
+    in_b = 1 if w.fp8 else 2
+    out_b = 4 if w.out == "f32" else 2
+    return tokens * w.H * w.d * (3 * in_b + out_b) + tokens * w.H * 4
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "io_aware_exact_attn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(wname):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counters, valid only while the kernel sources are unchanged."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{wname}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p, encoding="utf-8") as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, O_gpu, budget_s):
+    """The fp64 oracle, as it stands, on whole heads of the workload until about
+    ``budget_s`` seconds of CPU time are spent; scaled to TFLOP/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count()
+    if w.fp8:
+        qd = oracle.dequantize_e4m3_blocks(inp["q"], inp["q_scale"])
+        kd = oracle.dequantize_e4m3_blocks(inp["k"], inp["k_scale"])
+        vd = oracle.dequantize_e4m3_blocks(inp["v"], inp["v_scale"])
+    else:
+        qd, kd, vd = (oracle.bf16_decode(inp[t]) for t in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    done, f_done, max_err = 0, 0.0, 0.0
+    for h in range(w.H):
+        if w.varlen:
+            cu = inp["cu_seqlens"]
+            O, _ = oracle.attention(qd[:, h:h + 1], kd[:, h:h + 1], vd[:, h:h + 1], w.scale,
+                                    causal=w.causal, cu_seqlens=cu)
+            f_done += flops(w, inp["lengths"]) / w.H
+            max_err = max(max_err, float(np.abs(O[:, 0] - O_gpu[:, h]).max()))
+        else:
+            O, _ = oracle.attention(qd[:, :, h:h + 1], kd[:, :, h:h + 1], vd[:, :, h:h + 1], w.scale,
+                                    causal=w.causal)
+            f_done += flops(w) / w.H
+            max_err = max(max_err, float(np.abs(O[:, :, 0] - O_gpu[:, :, h]).max()))
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": f_done / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {w.H} heads, every row, fp64 numpy oracle; {dt:.1f} s",
+            "seconds": round(dt, 3), "max_abs_err_vs_gpu_on_sample": max_err}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the attention forward is built and timed on a single "
+              f"MI355X; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import io_aware_exact_attn_amd as ia
+    import workloads as W
+
+    w = W.workload(args.workload)
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def td(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        if a.dtype == np.uint8:
+            return torch.from_numpy(a).view(torch.float8_e4m3fn).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = td(inp["q"]), td(inp["k"]), td(inp["v"])
+    if w.varlen:
+        B, N = len(inp["lengths"]), w.N
+        o_shape, lse_shape = (N, w.H, w.d), (w.H, N)
+        cu = td(inp["cu_seqlens"])
+    else:
+        B, N = w.B, w.N
+        o_shape, lse_shape = (B, N, w.H, w.d), (B, w.H, N)
+        cu = None
+    o = torch.empty(o_shape, dtype=torch.float32 if w.out == "f32" else torch.bfloat16, device=dev)
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    if w.fp8:
+        qs, ks, vs = td(inp["q_scale"]), td(inp["k_scale"]), td(inp["v_scale"])
+
+        def step():
+            ia.attn_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, w.H, N, w.d, w.scale, int(w.causal),
+                            None, stream)
+        kname = ia.attn_kernel_name(w.d, int(w.causal), 0, 0, fp8=1)
+        dtype = "fp8"
+    else:
+        dt_code = ia.ATTN_BF16_OUT_F32 if w.out == "f32" else ia.ATTN_BF16
+
+        def step():
+            ia.attn_fwd(q, k, v, o, lse, B, w.H, N, w.d, w.scale, int(w.causal), cu, dt_code, stream)
+        kname = ia.attn_kernel_name(w.d, int(w.causal), int(w.varlen), dt_code)
+        dtype = "bf16"
+
+    # first launch (code-object load) timed on its own, then warm-up
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    per = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # per-launch spread (separate pass, each launch bracketed by events)
+    for _ in range(min(args.steps, 10)):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        step()
+        b_.record(stream)
+        b_.synchronize()
+        per.append(a_.elapsed_time(b_))
+
+    F = flops(w, inp.get("lengths"))
+    tflops = F / (ms * 1e-3) / 1e12
+    peak = PEAK[dtype]
+    traffic = traffic_from_profiles(w.name)
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded numpy PCG64 inputs of the workload's shape and distribution)",
+        "config": {"workload": w.name, "B": B, "H": w.H, "N": N, "d": w.d, "causal": w.causal,
+                   "packed": w.varlen, "out": w.out, "scale": w.scale, "flop_per_step": F,
+                   "kernel": kname},
+        "pct_of_peak": round(100 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes": algorithmic_bytes(w)},
+        "timing": {"first_launch_ms": round(first_ms, 3), "wall_ms_timed_region": round(wall_ms, 3),
+                   "per_launch_ms_min": round(min(per), 5), "per_launch_ms_median": round(float(np.median(per)), 5),
+                   "per_launch_ms_max": round(max(per), 5)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        O_gpu = o.float().cpu().numpy().astype(np.float64)
+        res["cpu_baseline"] = cpu_baseline(w, inp, O_gpu, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * attn.h - exact attention forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (all entry points):
+ *
+ *     O   = softmax(scale * Q K^T + mask) V
+ *     LSE = per query row, ln( sum_j exp(scale * q_i . k_j + mask_ij) )
+ *
+ * where mask_ij is 0 for a visible key and -inf otherwise.  This is the
+ * attention of "Flash Attention và IO" (aihero.vn): each query row is compared
+ * with the keys, the scores are normalised with a softmax, and the values are
+ * summed with those weights.  The kernels compute it tile by tile with the
+ * running-statistics softmax of that page's section "Softmax qua nhiều khối cần
+ * thống kê chạy" (running maximum m, normaliser l, weighted sum u; the result
+ * is u / l), so the N x N score and probability matrices never reach device
+ * memory.  The page's section "Tiling giữ công việc ở gần nơi tính" makes the
+ * result exact: it differs from the plain definition only by floating-point
+ * evaluation order.  Loop order and sequence-level parallelism follow the
+ * FlashAttention-2 part of "FlashAttention, pelatihan multi-GPU, dan
+ * kuantisasi bobot", section 1 (Q blocks outer, K/V blocks inner, one
+ * normalisation at the end).
+ *
+ * Masks
+ *   causal = 0   every key of the sequence is visible.
+ *   causal = 1   key j is visible to query i iff j <= i (the same sequence
+ *                length for queries and keys, aligned at the first token).
+ *   cu_seqlens   packed documents: a query sees only keys of its own document
+ *                (combined with the causal rule inside the document when
+ *                causal = 1).  Packed layouts follow the document-local,
+ *                no-repacking design of "FLAMIA: Blackwell Üzerinde Hızlı ve
+ *                Nedensel Olarak Güvenli Eğitim İçin Flash Mikro-Ölçeklemeli
+ *                Dikkat Mekanizması", section "FLAMIA Mimarisi ve Temel
+ *                Tasarım İlkeleri".
+ *
+ * Layouts (row-major, contiguous, element strides implied by the sizes)
+ *   fixed length (cu_seqlens == NULL):
+ *     q, k, v, o : [B][N][H][d]          lse : [B][H][N]  (fp32)
+ *   packed (cu_seqlens != NULL):  B = number of documents, N = total tokens
+ *     q, k, v, o : [N][H][d]             lse : [H][N]     (fp32)
+ *     cu_seqlens : B + 1 int32 prefix offsets in DEVICE memory,
+ *                  cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = N.
+ *
+ * Supported set
+ *   d in {64, 128}; B, H, N >= 1; B * H * N < 2^31 (elements per tensor
+ *   < 2^31 * d); scale finite (any sign, zero allowed).
+ *   attn_fwd:     bf16 q/k/v; o bf16 (ATTN_BF16) or fp32 (ATTN_BF16_OUT_F32).
+ *   attn_fwd_fp8: e4m3 q/k/v with per-128-token block scales, o bf16, d = 128,
+ *                 fixed length only (cu_seqlens must be NULL).
+ *   Anything else returns an error; there is no fallback path.
+ *
+ * Ownership and concurrency
+ *   Every pointer is device memory owned by the caller (except that `stream`
+ *   is a HIP stream handle, NULL for the null stream).  The library allocates
+ *   nothing, keeps no pointer after returning, has no mutable global state
+ *   and may be called from several threads at once.  Every pointer must be
+ *   16-byte aligned.  Inputs are never written; o and lse are fully
+ *   overwritten.
+ *
+ * Errors
+ *   The return value is an attn_status.  A nonzero status means nothing was
+ *   enqueued and the outputs are untouched, except ATTN_ERR_HIP, which reports
+ *   a failed launch (the HIP error of the launch).  Calls return as soon as the
+ *   work is enqueued on `stream`; device-side problems (including invalid
+ *   cu_seqlens contents, which the host never reads) show at the caller's
+ *   next synchronisation and leave the outputs undefined.
+ */
+#ifndef IAEA_ATTN_H
+#define IAEA_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_API __attribute__((visibility("default")))
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,         /* a required pointer is NULL                         */
+    ATTN_ERR_SHAPE = 2,        /* B, H or N < 1, or the tensors are too large        */
+    ATTN_ERR_UNSUPPORTED = 3,  /* d, dtype, causal flag or packed fp8 not supported  */
+    ATTN_ERR_SCALE = 4,        /* scale is NaN or infinite                           */
+    ATTN_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned                   */
+    ATTN_ERR_HIP = 6           /* the kernel launch failed                           */
+} attn_status;
+
+typedef enum {
+    ATTN_BF16 = 0,             /* bf16 q/k/v, bf16 o (round to nearest even)         */
+    ATTN_BF16_OUT_F32 = 1,     /* bf16 q/k/v, fp32 o                                 */
+    ATTN_FP8_E4M3 = 2          /* e4m3 operands: use attn_fwd_fp8 (attn_fwd rejects) */
+} attn_dtype;
+
+/*
+ * attn_fwd - bf16 exact attention forward.
+ *   q, k, v     bf16 inputs, layout above.
+ *   o           output, bf16 or fp32 per `dtype`, layout above.
+ *   lse         fp32 per-row log-sum-exp (natural log, of the scaled and
+ *               masked scores), layout above.
+ *   B, H, N, d  sizes (packed: B documents, N total tokens).
+ *   scale       multiplies q . k before the softmax (for example 1/sqrt(d)).
+ *   causal      0 or 1.
+ *   cu_seqlens  NULL for fixed length; else device int32[B + 1] (packed).
+ *   dtype       ATTN_BF16 or ATTN_BF16_OUT_F32.
+ *   stream      HIP stream (hipStream_t) to enqueue on.
+ */
+ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int N, int d, float scale, int causal,
+                      const int32_t* cu_seqlens, int dtype, void* stream);
+
+/*
+ * attn_fwd_fp8 - block-scaled fp8 exact attention forward (d = 128, fixed
+ * length).  The FP8 path with per-tile scales follows the FlashAttention-3
+ * part of "FlashAttention, pelatihan multi-GPU, dan kuantisasi bobot",
+ * section 1 (block quantisation: each tile carries its own scale); the scale
+ * blocks never mix tokens of different 128-token blocks, the causal-leakage
+ * concern of the FLAMIA page (sections "Uzun Bağlamlarda Dikkat (Attention)
+ * Maliyeti ve Blackwell Mimarisi" and "FLAMIA Mimarisi ve Temel Tasarım
+ * İlkeleri").
+ *   q, k, v     OCP e4m3 ("e4m3fn") bytes, [B][N][H][128].
+ *   q_scale, k_scale, v_scale
+ *               fp32 [B][H][ceil(N / 128)]: token t of (b, h) has the value
+ *               e4m3(byte) * scale[b][h][t / 128].
+ *   o           bf16 [B][N][H][128];  lse fp32 [B][H][N].
+ *   The probabilities P enter the P.V contraction as e4m3 as well, in tiles
+ *   of 128 query rows with a fixed scale of 2^8 (P <= 1 after the running
+ *   maximum is subtracted, so no data-dependent scale is needed; a data-
+ *   dependent one would read future keys).  P is carried as two e4m3 terms
+ *   (P ~ hi + lo, hi = e4m3(P * 2^8) / 2^8, lo = e4m3((P - hi) * 2^12) / 2^12);
+ *   the normaliser l is summed from the unquantised fp32 P.
+ *   Other arguments as attn_fwd; cu_seqlens must be NULL.
+ */
+ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
+                          const float* q_scale, const float* k_scale, const float* v_scale,
+                          void* o, float* lse, int B, int H, int N, int d, float scale,
+                          int causal, const int32_t* cu_seqlens, void* stream);
+
+/* attn_status_str - static, NUL-terminated description of a status code
+ * (unknown codes give "unknown status").  Never NULL; do not free. */
+ATTN_API const char* attn_status_str(int status);
+
+/* attn_kernel_name - static name of the kernel attn_fwd / attn_fwd_fp8 would
+ * launch for these arguments ("" when the arguments are not supported), so a
+ * caller can confirm which code path runs.  fp8 != 0 selects attn_fwd_fp8. */
+ATTN_API const char* attn_kernel_name(int d, int causal, int packed, int dtype, int fp8);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IAEA_ATTN_H */

