@@ -8,6 +8,7 @@ namespace iaea {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -57,10 +58,20 @@ __device__ __forceinline__ float wave_max_half_swap(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
 }
 
+// acc + lo(pair) + hi(pair) for a packed bf16 pair (v_dot2 against (1, 1)).
+// The pair must be a scalar register value: extracting it from a vector
+// makes the compiler read element 0 for every element.  Kept as a builtin
+// (not asm) so the compiler inserts the wait states its result needs.
+__device__ __forceinline__ float sum2_bf16(uint32_t pair, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a;
-  __bf16 y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  // one v_cvt_pk_bf16_f32 (round to nearest even)
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 }  // namespace iaea

@@ -104,21 +104,39 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, int lb, int& h, in
   }
 }
 
-template <int D, int QB, int NW, bool CAUSAL, bool PACKED, bool OUT_F32>
-__global__ void __launch_bounds__(NW * 64)
+// Compile-time shape of a kernel instance: head dimension D, query blocks of
+// 32 rows per wave QB, waves per workgroup NW, the occupancy the register
+// budget is sized for (waves per SIMD), and the instruction interleave.
+// The running state is rescaled only when the running maximum grows by more
+// than 2^kLazyLog2: u / l does not depend on the reference maximum, so this
+// is exact up to rounding and only lets P reach 2^kLazyLog2.
+template <int D_, int QB_, int NW_, int WPE_, bool SCHED_ = false, int VPM_ = 6>
+struct BfCfg {
+  static constexpr int D = D_, QB = QB_, NW = NW_, WPE = WPE_;
+  static constexpr bool SCHED = SCHED_;   // hand interleaving of QK^T MFMAs and softmax VALU
+  static constexpr int VPM = VPM_;        // VALU instructions per MFMA in that interleave
+};
+
+constexpr float kLazyLog2 = 8.f;
+
+template <int P> struct Parity { static constexpr int value = P; };
+
+template <class Cfg, bool CAUSAL, bool PACKED, bool OUT_F32>
+__global__ void __launch_bounds__(Cfg::NW * 64) __attribute__((amdgpu_waves_per_eu(Cfg::WPE)))
 attn_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int D = Cfg::D, QB = Cfg::QB, NW = Cfg::NW;
   constexpr int BN = 64;                 // keys per tile
   constexpr int QW = 32 * QB;            // query rows per wave
   constexpr int BM = QW * NW;            // query rows per workgroup
-  constexpr int G = D / 8;               // 16-byte granules per row
-  constexpr int NT = NW * 64;
-  constexpr int TILE = BN * D * 2;       // bytes of one K or V tile
-  constexpr int LOADS = BN * G / NT;     // granules per thread per tile
+  constexpr int ROWB = D * 2;            // bytes of one K/V row
+  constexpr int TILE = BN * ROWB;        // bytes of one K or V tile
+  constexpr int CPW = TILE / 1024 / NW;  // 1 KB direct-load chunks per wave per tile
   constexpr int DC = D / 16;             // k-steps of the QK^T MFMA
   constexpr int DB = D / 32;             // 32-wide blocks of d in O
-  static_assert(LOADS * NT == BN * G, "tile must split evenly over the threads");
+  static_assert(CPW * NW * 1024 == TILE, "tile must split into whole 1 KB chunks per wave");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+  // K(j) lives in buffer j % 2, V(j) in buffer 2 + j % 2
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
 
   int h, b, seq_start, seq_len, qblk;
   if (!decode_work<BM, CAUSAL, PACKED>(a, logical_block(blockIdx.x, a.per_xcd), h, b,
@@ -126,7 +144,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     return;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5;              // which half of the wave
   const int l32 = lane & 31;
   const int q0 = qblk * BM;
@@ -158,165 +176,254 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  // ---- K/V tile staging: global -> registers -> swizzled LDS
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int it) {
-    const int kv0 = it * BN;
+  // ---- K/V tiles: global -> LDS directly (global_load_lds_dwordx4).  Lane i of
+  // a wave writes LDS bytes [chunk + 16 i, chunk + 16 i + 16); it fetches the
+  // logical granule that the swizzle places there.  The per-lane byte offset
+  // inside a tile is loop-invariant; the tile base is wave-uniform.  Rows past
+  // the end of the sequence re-read its last row: those keys are masked and
+  // their weights are 0.
+  uint32_t lane_off[CPW];
+  int lane_row[CPW];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int idx = threadIdx.x + i * NT;
-      const int row = idx / G, g = idx % G;
-      const int t = kv0 + row;
-      const bool ok = t < seq_len;
-      const int64_t off = (int64_t)(seq_start + (ok ? t : 0)) * rs + head_off + g * 8;
-      kreg[i] = ok ? *(const u32x4*)(kg + off) : (u32x4){0u, 0u, 0u, 0u};
-      vreg[i] = ok ? *(const u32x4*)(vg + off) : (u32x4){0u, 0u, 0u, 0u};
+  for (int cc = 0; cc < CPW; ++cc) {
+    const int byte = (wave * CPW + cc) * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int g = ((byte % ROWB) >> 4) ^ swz<D>(row);
+    lane_row[cc] = row;
+    lane_off[cc] = (uint32_t)(((int64_t)row * rs + head_off + g * 8) * 2);
+  }
+  auto issue_tile = [&](const uint16_t* __restrict__ src, int buf, int j) {
+    const int kv0 = j * BN;
+    const char* base = (const char*)(src + (int64_t)(seq_start + kv0) * rs);
+    char* dst = smem + buf * TILE + wave * CPW * 1024;
+    if (kv0 + BN <= seq_len) {
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc)
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(base + lane_off[cc]),
+                                         (IAEA_LDS void*)(dst + cc * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc) {
+        const int over = max(0, kv0 + lane_row[cc] - (seq_len - 1));
+        const uint32_t off = lane_off[cc] - (uint32_t)((int64_t)over * rs * 2);
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(base + off),
+                                         (IAEA_LDS void*)(dst + cc * 1024), 16, 0, 0);
+      }
     }
   };
-  auto lstore = [&](int stage) {
-    char* kt = smem + stage * 2 * TILE;
-    char* vt = kt + TILE;
+
+  // ---- loop-invariant LDS read offsets; buffer bases and the steps over key
+  // blocks are compile-time immediates.  K fragment (A operand of S^T): row
+  // kb * 32 + l32, granule 2 * dc + hl.  V^T fragment (ds_read_b64_tr_b16): in
+  // each 16-lane group, source lane s points at key row 4 * half + s / 4 (and
+  // + 8 for the upper four keys) and d offset 4 * (s % 4) of the group's 16 d
+  // columns; lane i then holds d column i of four consecutive keys.  The
+  // swizzle repeats every 16 rows, so whole 16-row steps stay immediates.
+  uint32_t koff[DC];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int idx = threadIdx.x + i * NT;
-      const int row = idx / G, g = idx % G;
-      *(u32x4*)(kt + lds_off<D>(row, g)) = kreg[i];
-      *(u32x4*)(vt + lds_off<D>(row, g)) = vreg[i];
+  for (int dc = 0; dc < DC; ++dc) koff[dc] = l32 * ROWB + (((2 * dc + hl) ^ swz<D>(l32)) << 4);
+  uint32_t voff[2][DB];
+  {
+    const int g16 = lane >> 4;
+    const int v_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+    const int v_dcol = 16 * (g16 & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = v_row + 8 * hi;
+        const int d = db * 32 + v_dcol;
+        voff[hi][db] = row * ROWB + (((d >> 3) ^ swz<D>(row)) << 4) + (d & 7) * 2;
+      }
+  }
+
+  auto qk = [&](auto kbuf_tag, f32x16 (&s)[QB][2]) {
+    constexpr int KB = decltype(kbuf_tag)::value;
+    const char* kt = smem + KB * TILE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 kf = *(const bf16x8*)(kt + kb * 32 * ROWB + koff[dc]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              kf, qf[qb][dc], dc == 0 ? (f32x16){} : s[qb][kb], 0, 0, 0);
+      }
     }
   };
 
   f32x16 oacc[QB][DB];
-  float m_run[QB], l_run[QB];
+  float m_run[QB], l_run[QB], lx_run[QB];   // reference max, rounded and exact sums
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
     l_run[qb] = 0.f;
+    lx_run[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[qb][db] = (f32x16){};
   }
 
-  // lane-constant parts of the transposed V read (ds_read_b64_tr_b16): in each
-  // 16-lane group, source lane s points at key row 4*half + s/4 and d offset
-  // 4*(s%4) of the group's 16 d columns; lane i then holds d column i of four
-  // consecutive keys.
-  const int g16 = lane >> 4;
-  const int v_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
-  const int v_dcol = 16 * (g16 & 1) + 4 * (lane & 3);
-
-  if (n_iter > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n_iter; ++it) {
-    if (it + 1 < n_iter) gload(it + 1);
-    if (it < wave_iters) {
-      const char* kt = smem + (it & 1) * 2 * TILE;
-      const char* vt = kt + TILE;
-      const int kv0 = it * BN;
-
-      // S^T[key][query] for two 32-key halves of the tile
-      f32x16 s[QB][2];
+  // P = exp2(s * c - ms) for one 32-query block, rounded to bf16 and packed as
+  // the four 16-key B operands of O^T += V^T P^T.  Also returns this lane's
+  // sums of the weights: lr of the bf16-rounded ones (those enter P.V, so
+  // u / lr is an exact weighted average of them: a dominant key returns its
+  // value) and lx of the unrounded ones (for the LSE).
+  auto weights = [&](const f32x16 (&sq)[2], float ms, bf16x8 (&pq)[4], float& lr, float& lx) {
+    float r0 = 0.f, r1 = 0.f, x0 = 0.f, x1 = 0.f;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][0] = s[qb][1] = (f32x16){};
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 w;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const bf16x8 kf = *(const bf16x8*)(kt + lds_off<D>(kb * 32 + l32, dc * 2 + hl));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][dc], s[qb][kb], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = fast_exp2(__builtin_fmaf(sq[kb][8 * c2 + 2 * j], c, -ms));
+          const float p1 = fast_exp2(__builtin_fmaf(sq[kb][8 * c2 + 2 * j + 1], c, -ms));
+          const uint32_t pk = pack_bf16x2(p0, p1);
+          if (j & 1) { r1 = sum2_bf16(pk, r1); x1 += p0 + p1; }
+          else       { r0 = sum2_bf16(pk, r0); x0 += p0 + p1; }
+          w[j] = pk;
         }
+        pq[kb * 2 + c2] = __builtin_bit_cast(bf16x8, w);
       }
+    lr = r0 + r1;
+    lx = x0 + x1;
+  };
 
-      // mask keys past the end of the sequence and, when causal, future keys
+  // one pipeline step for tile `it` (parity P): S(it) is in s_cur; S(it + 1)
+  // goes to s_nxt on the matrix cores while S(it)'s softmax runs on the VALU
+  auto step = [&](auto par, int it, f32x16 (&s_cur)[QB][2], f32x16 (&s_nxt)[QB][2]) {
+    constexpr int P = decltype(par)::value;
+    // prefetch K two tiles ahead into the buffer K(it) used, V one tile ahead
+    if (it + 2 < n_iter) issue_tile(kg, P, it + 2);
+    if (it + 1 < n_iter) issue_tile(vg, 2 + (P ^ 1), it + 1);
+
+    if (it < wave_iters) {
+      const int kv0 = it * BN;
+      // mask keys past the end of the sequence and, when causal, future keys:
+      // the key of register r is kv0 + kb*32 + (r/4)*8 + half*4 + r%4
       const bool edge = (kv0 + BN > seq_len) || (CAUSAL && kv0 + BN - 1 > wq0);
       if (edge) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const int qi = wq0 + qb * 32 + l32;
+          const int lim = (CAUSAL ? min(wq0 + qb * 32 + l32, seq_len - 1) : seq_len - 1) - (kv0 + hl * 4);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kj = kv0 + kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-              if (kj >= seq_len || (CAUSAL && kj > qi)) s[qb][kb][r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) s_cur[qb][kb][r] = -INFINITY;
         }
       }
 
-      // running-statistics softmax update
+      // unconditional, so the matrix work shares a basic block with the
+      // softmax below and the two can be interleaved; past the wave's last
+      // tile the result is never used
+      qk(Parity<P ^ 1>{}, s_nxt);
+
+      // running-statistics softmax update of this tile.  The weights are first
+      // formed against the current reference maximum m (no dependence on this
+      // tile's maximum, so they overlap the MFMAs above).  The reference moves
+      // to m_new = max(m, m_b) - and the old l and u are scaled by
+      // exp(m - m_new) - only when some row of the wave grew by more than
+      // 2^kLazyLog2 (always on a row's first tile, where m = -inf); then the
+      // weights are formed again.  u / l does not depend on the reference.
+      bf16x8 pf[QB][4];
+      float mx[QB], lr[QB], lx[QB];
+      bool move = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = s[qb][0][0];
+        const float ms = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
+        weights(s_cur[qb], ms, pf[qb], lr[qb], lx[qb]);
+        float m = fmaxf(s_cur[qb][0][0], s_cur[qb][1][0]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, fmaxf(s_cur[qb][0][r], s_cur[qb][1][r]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                         false, false);
+        mx[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        move |= (mx[qb] - m_run[qb]) * c > kLazyLog2 || m_run[qb] == -INFINITY;
+      }
+      if constexpr (Cfg::SCHED) {
+        // interleave: one K-fragment read, one MFMA of S(it + 1), then a slice
+        // of this tile's softmax, so the VALU runs under the matrix cores
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        mx = wave_max_half_swap(mx);
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float ms_new = (m_new == -INFINITY) ? 0.f : m_new * c;
-        const float alpha = (m_run[qb] == -INFINITY) ? 0.f : fast_exp2(m_run[qb] * c - ms_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
+        for (int i = 0; i < 2 * DC * QB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, Cfg::VPM, 0);   // VALU
+        }
+      }
+      if (__ballot(move) != 0) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
-        float lsum = 0.f;
+        for (int qb = 0; qb < QB; ++qb) {
+          const float m_new = fmaxf(m_run[qb], mx[qb]);
+          const float alpha = (m_run[qb] == -INFINITY) ? 0.f : fast_exp2((m_run[qb] - m_new) * c);
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+          lx_run[qb] *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+          const float ms = (m_new == -INFINITY) ? 0.f : m_new * c;
+          weights(s_cur[qb], ms, pf[qb], lr[qb], lx[qb]);
+        }
+      }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, -ms_new));
-            s[qb][kb][r] = p;
-            lsum += p;
-          }
-        l_run[qb] += lsum;
+      for (int qb = 0; qb < QB; ++qb) {
+        l_run[qb] += lr[qb];
+        lx_run[qb] += lx[qb];
       }
 
       // O^T += V^T P^T over four 16-key chunks
+      const char* vt = smem + (2 + P) * TILE;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          bf16x8 pf[QB];
+        for (int db = 0; db < DB; ++db) {
+          const bf16x4 lo = ds_read_tr16(vt + kc * 16 * ROWB + voff[0][db]);
+          const bf16x4 hi = ds_read_tr16(vt + kc * 16 * ROWB + voff[1][db]);
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            u32x4 w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              w[j] = pack_bf16x2(s[qb][kb][8 * c2 + 2 * j], s[qb][kb][8 * c2 + 2 * j + 1]);
-            pf[qb] = __builtin_bit_cast(bf16x8, w);
-          }
-          const int row = kb * 32 + 16 * c2 + v_row;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + v_dcol;
-            const bf16x4 lo = ds_read_tr16(vt + lds_off<D>(row, d >> 3) + (d & 7) * 2);
-            const bf16x4 hi = ds_read_tr16(vt + lds_off<D>(row + 8, d >> 3) + (d & 7) * 2);
-            const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], oacc[qb][db], 0, 0, 0);
-          }
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kc], oacc[qb][db], 0, 0, 0);
         }
       }
     }
-    if (it + 1 < n_iter) lstore((it + 1) & 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  // prologue: K(0), K(1), V(0) resident, S(0) computed
+  if (n_iter > 0) {
+    issue_tile(kg, 0, 0);
+    issue_tile(vg, 2, 0);
+    if (n_iter > 1) issue_tile(kg, 1, 1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 sa[QB][2], sb[QB][2];
+  if (wave_iters > 0) qk(Parity<0>{}, sa);
+  __syncthreads();   // every wave has read K(0) before K(2) replaces it
+
+  for (int it = 0; it < n_iter; it += 2) {
+    step(Parity<0>{}, it, sa, sb);
+    if (it + 1 < n_iter) step(Parity<1>{}, it + 1, sb, sa);
   }
 
   // ---- epilogue: O = u / l, LSE = ln2 * (m * c + log2 l)
   const int64_t lse_base = PACKED ? ((int64_t)h * a.N + seq_start) : ((int64_t)(b * a.H + h) * a.N);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[qb]),
+                                                     __float_as_uint(l_run[qb]), false, false);
+    const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const auto swx = __builtin_amdgcn_permlane32_swap(__float_as_uint(lx_run[qb]),
+                                                      __float_as_uint(lx_run[qb]), false, false);
+    const float lx_tot = __uint_as_float(swx[0]) + __uint_as_float(swx[1]);
     const int t = wq0 + qb * 32 + l32;
     if (t >= seq_len) continue;
     const bool any = l_tot > 0.f;
     const float inv = any ? 1.f / l_tot : 0.f;
-    if (hl == 0) a.lse[lse_base + t] = any ? kLn2 * (m_run[qb] * c + __log2f(l_tot)) : -INFINITY;
+    if (hl == 0) a.lse[lse_base + t] = any ? kLn2 * (m_run[qb] * c + __log2f(lx_tot)) : -INFINITY;
     const int64_t orow = (int64_t)(seq_start + t) * rs + head_off;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -338,9 +445,10 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 // launch
 // ---------------------------------------------------------------------------
 
-template <int D, int QB, int NW, bool CAUSAL, bool PACKED, bool OUT_F32>
+template <class Cfg, bool CAUSAL, bool PACKED, bool OUT_F32>
 static hipError_t launch_one(FwdArgs a, hipStream_t st) {
-  constexpr int BM = 32 * QB * NW;
+  constexpr int NW = Cfg::NW;
+  constexpr int BM = 32 * Cfg::QB * NW;
   if (PACKED) {
     a.slots = (a.N + BM - 1) / BM + a.B;
     a.n_work = a.H * a.slots;
@@ -352,21 +460,20 @@ static hipError_t launch_one(FwdArgs a, hipStream_t st) {
   a.per_xcd = grid / kXcds;
   void* args[] = {&a};
   // the launch's own status (hipGetLastError could report an earlier, unrelated call)
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<D, QB, NW, CAUSAL, PACKED, OUT_F32>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<Cfg, CAUSAL, PACKED, OUT_F32>),
                          dim3(grid), dim3(NW * 64), args, 0, st);
 }
 
-// Tile shape per head dimension: queries per wave (32 * QB) and waves per
-// workgroup.
+// Kernel instance per head dimension.
 template <int D> struct BfTile;
-template <> struct BfTile<128> { static constexpr int QB = 1, NW = 4; };
-template <> struct BfTile<64>  { static constexpr int QB = 1, NW = 4; };
+template <> struct BfTile<128> { using Cfg = BfCfg<128, 1, 4, 2, false>; };
+template <> struct BfTile<64>  { using Cfg = BfCfg<64, 1, 4, 2, false>; };
 
 template <int D, bool CAUSAL, bool PACKED>
 static hipError_t launch_d(const FwdArgs& a, bool out_f32, hipStream_t st) {
-  constexpr int QB = BfTile<D>::QB, NW = BfTile<D>::NW;
-  return out_f32 ? launch_one<D, QB, NW, CAUSAL, PACKED, true>(a, st)
-                 : launch_one<D, QB, NW, CAUSAL, PACKED, false>(a, st);
+  using Cfg = typename BfTile<D>::Cfg;
+  return out_f32 ? launch_one<Cfg, CAUSAL, PACKED, true>(a, st)
+                 : launch_one<Cfg, CAUSAL, PACKED, false>(a, st);
 }
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, int d, bool causal, bool packed, bool out_f32,
@@ -380,7 +487,9 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, int d, bool causal, bool packe
 }
 
 int bf16_rows_per_workgroup(int d) {
-  return d == 128 ? 32 * BfTile<128>::QB * BfTile<128>::NW : 32 * BfTile<64>::QB * BfTile<64>::NW;
+  using C128 = BfTile<128>::Cfg;
+  using C64 = BfTile<64>::Cfg;
+  return d == 128 ? 32 * C128::QB * C128::NW : 32 * C64::QB * C64::NW;
 }
 
 }  // namespace iaea
