@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run a plain device copy of MIB MiB (the "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -126,6 +129,18 @@ def main():
     import torch
     import io_aware_exact_attn_amd as ia
     import workloads as W
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_launch": n * 4,
+                          "copy_calibration_bytes_written_per_launch": n * 4,
+                          "launches": args.warmup + args.steps}), flush=True)
+        return
 
     w = W.workload(args.workload)
     inp = W.make_inputs(w)
