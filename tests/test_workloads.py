@@ -125,3 +125,14 @@ def test_make_inputs_heads_subset_is_prefix():
 def test_scale_is_fp32_rounded():
     assert W.workload(2).scale == float(np.float32(1 / np.sqrt(128)))
     assert W.workload(1).scale == 0.125
+
+
+def test_quantize_partial_last_block():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((1, 300, 2, 8)).astype(np.float32)
+    q, s = W.quantize_e4m3_blocks(x)
+    assert q.shape == x.shape and s.shape == (1, 2, 3)
+    # the partial block (tokens 256..299) is scaled by its own amax only
+    assert s[0, 1, 2] == np.float32(np.abs(x[0, 256:, 1]).max() / np.float32(448))
+    q2, s2 = W.quantize_e4m3_blocks(x[:, :256])
+    assert np.array_equal(q2, q[:, :256]) and np.array_equal(s2, s[:, :, :2])

@@ -170,24 +170,24 @@ def quantize_e4m3_blocks(x: np.ndarray, block: int = FP8_BLOCK):
     One fp32 scale per (batch, head, ``block`` consecutive tokens) over all d:
     s = amax / 448 (s = 1 when the block is all zero), x_hat = e4m3(x / s)
     with the division done in fp32.  A scale is computed from its own block's
-    tokens only, so no scale mixes tokens of different blocks.
+    tokens only, so no scale mixes tokens of different blocks; a last partial
+    block uses just its own tokens.
 
-    Returns (bytes uint8 [B, N, H, d], scales float32 [B, H, N // block]).
-    N must be a multiple of ``block``.
+    Returns (bytes uint8 [B, N, H, d], scales float32 [B, H, ceil(N / block)]).
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     B, N, H, d = x.shape
-    if N % block:
-        raise ValueError("N must be a multiple of the scale block")
-    nb = N // block
-    xb = x.reshape(B, nb, block, H, d)
+    nb = -(-N // block)
+    pad = nb * block - N
+    xp = np.concatenate([x, np.zeros((B, pad, H, d), np.float32)], axis=1) if pad else x
+    xb = xp.reshape(B, nb, block, H, d)
     amax = np.abs(xb).max(axis=(2, 4))                     # [B, nb, H]
     s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
     s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
     y = (xb / s[:, :, None, :, None]).astype(np.float32)
-    q = e4m3_encode_rne_sat(y).reshape(B, N, H, d)
+    q = e4m3_encode_rne_sat(y).reshape(B, nb * block, H, d)[:, :N]
     scales = np.ascontiguousarray(s.transpose(0, 2, 1))    # [B, H, nb]
-    return q, scales
+    return np.ascontiguousarray(q), scales
 
 
 # ---------------------------------------------------------------------------
