@@ -79,6 +79,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,         /* a required pointer is NULL                         */
     ATTN_ERR_SHAPE = 2,        /* B, H or N < 1, or the tensors are too large        */
+                               /* (B*N*H >= 2^31; bf16: H*d > 2^24)                  */
     ATTN_ERR_UNSUPPORTED = 3,  /* d, dtype, causal flag or packed fp8 not supported  */
     ATTN_ERR_SCALE = 4,        /* scale is NaN or infinite                           */
     ATTN_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned                   */

@@ -53,6 +53,8 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, floa
   if (st != ATTN_OK) return st;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (dtype != ATTN_BF16 && dtype != ATTN_BF16_OUT_F32) return ATTN_ERR_UNSUPPORTED;
+  // a 64-row K/V tile of all heads (64 * H * d * 2 bytes) is addressed with 32-bit offsets
+  if ((int64_t)H * d > ((int64_t)1 << 24)) return ATTN_ERR_SHAPE;
   if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
   if (cu_seqlens) {
     // packed: B documents over N tokens; the grid has ceil(N / BM) + B slots per head

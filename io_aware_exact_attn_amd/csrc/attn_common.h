@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -23,6 +24,9 @@ constexpr int kWave = 64;
 constexpr int kXcds = 8;          // MI355X: workgroups go round-robin to 8 XCDs
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Word 3 of a raw (stride 0) buffer resource on CDNA: 32-bit data format,
+// out-of-range dwords read as zero.
+constexpr int kBufferFlags = 0x00020000;
 
 // Kernel arguments shared by the bf16 and fp8 paths.
 struct FwdArgs {
@@ -52,20 +56,6 @@ __device__ __forceinline__ int logical_block(int bid, int per_xcd) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ float wave_max_half_swap(float x) {
-  // combine lanes l and l ^ 32 (the two halves of a 32x32 MFMA column)
-  return fmaxf(x, __shfl_xor(x, 32));
-}
-
-// acc + lo(pair) + hi(pair) for a packed bf16 pair (v_dot2 against (1, 1)).
-// The pair must be a scalar register value: extracting it from a vector
-// makes the compiler read element 0 for every element.  Kept as a builtin
-// (not asm) so the compiler inserts the wait states its result needs.
-__device__ __forceinline__ float sum2_bf16(uint32_t pair, float acc) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
-}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   // one v_cvt_pk_bf16_f32 (round to nearest even)

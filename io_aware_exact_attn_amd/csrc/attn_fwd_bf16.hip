@@ -1,26 +1,31 @@
 // bf16 exact attention forward for gfx950 (MI355X).
 //
-// One workgroup owns BM = NW * 32 * QB query rows of one (sequence, head) and
-// streams that head's keys and values through LDS in tiles of 64 rows: query
-// blocks are the outer (parallel) loop, key/value blocks the inner loop, the
-// order of the FlashAttention-2 part of "FlashAttention, pelatihan multi-GPU,
-// dan kuantisasi bobot" (section 1).  Per query row the kernel keeps the
-// running maximum m, the normaliser l and the weighted value sum u of the
-// section "Softmax qua nhiều khối cần thống kê chạy" of "Flash Attention và
-// IO"; a new tile with maximum m_b moves m to max(m, m_b), scales the old l
-// and u by exp(m - m_new) and adds exp(s - m_new) and exp(s - m_new) * v.  The
-// division u / l happens once, after the last tile (the deferred rescale of
-// the FlashAttention-2 part).  Scores and probabilities live only in
-// registers.
+// One workgroup owns BM = 256 query rows (8 waves of 32) of one (sequence,
+// head) and streams that head's keys and values through LDS in tiles of 64
+// rows: query blocks are the outer (parallel) loop, key/value blocks the
+// inner loop, the order of the FlashAttention-2 part of "FlashAttention,
+// pelatihan multi-GPU, dan kuantisasi bobot" (section 1).  Per query row the
+// kernel keeps the running maximum m, the normaliser l and the weighted value
+// sum u of the section "Softmax qua nhiều khối cần thống kê chạy" of "Flash
+// Attention và IO"; when m moves to m_new the old l and u are scaled by
+// exp(m - m_new).  The division u / l happens once, after the last tile (the
+// deferred rescale of the FlashAttention-2 part).  Scores and probabilities
+// live only in registers.
 //
 // MI355X mapping
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: with keys and
-//    d on the MFMA rows, every lane owns one query column, so the row max,
-//    the row sum, the rescale and the final 1/l are per-lane scalars, and the
-//    only cross-lane step is one exchange between lanes l and l ^ 32.
-//  * Q stays in VGPRs for the whole loop; K and V tiles are loaded with
-//    128-bit coalesced global loads into double-buffered LDS (one barrier per
-//    tile); V^T fragments come from ds_read_b64_tr_b16 transposed LDS reads.
+//    d on the MFMA rows, every lane owns one query column, so the softmax
+//    needs no cross-lane reduction except an exchange between lanes l and
+//    l ^ 32 for the rare rescale and at the end.
+//  * Two wave groups ping-pong on each SIMD (waves w and w + 4 share one):
+//    every wave alternates a matrix phase (MFMAs and LDS reads) with a
+//    softmax phase (VALU only), one group a phase behind the other, so one
+//    wave of each SIMD drives the matrix cores while the other drives the
+//    VALU.  A workgroup barrier ends every phase.
+//  * Q stays in VGPRs for the whole loop.  K and V tiles go from HBM straight
+//    to double-buffered LDS with buffer_load_dwordx4 ... lds (1 KB per
+//    instruction); the buffer size stops at the end of the sequence, so rows
+//    past it read as zeros.  V^T fragments come from ds_read_b64_tr_b16.
 //  * LDS rows are XOR-swizzled in 16-byte granules so both the K fragment
 //    reads and the transposed V reads are free of bank conflicts.
 //  * Causal: tiles above the diagonal are never loaded or computed, and
@@ -28,6 +33,8 @@
 //    the workgroups of one head on one XCD (L2) at a time.
 #include "attn_common.h"
 #include "attn_kernels.h"
+
+#include <utility>
 
 namespace iaea {
 
@@ -38,46 +45,57 @@ __device__ __forceinline__ int swz(int row) {
   else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-template <int D>
-__device__ __forceinline__ int lds_off(int row, int granule) {
-  return row * (D * 2) + ((granule ^ swz<D>(row)) << 4);
-}
-
-__device__ __forceinline__ bf16x4 ds_read_tr16(const char* p) {
+// The restrict-qualified pointer gives the read alias-scope metadata; without
+// it the compiler cannot tell it from the in-flight LDS DMA of other buffers
+// and waits for every outstanding tile load before it.
+__device__ __forceinline__ bf16x4 ds_read_tr16(const char* __restrict__ p) {
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IAEA_LDS s16x4*)(p));
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Compile-time shape of a kernel instance: head dimension D, query blocks of
-// 32 rows per wave QB, waves per workgroup NW, the occupancy the register
-// budget is sized for (waves per SIMD), and the instruction interleave.
-// The running state is rescaled only when the running maximum grows by more
-// than 2^kLazyLog2: u / l does not depend on the reference maximum, so this
-// is exact up to rounding and only lets P reach 2^kLazyLog2.
-template <int D_, int QB_, int NW_, int WPE_, bool SCHED_ = false, int VPM_ = 6>
+// Calls f(integral_constant<int, I>) for I = 0 .. N - 1, fully unrolled, so
+// register arrays are indexed by compile-time constants.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int P> using Parity = std::integral_constant<int, P>;
+
+// Compile-time shape of a kernel instance: head dimension D and how many
+// MFMA steps ahead of its use an LDS operand fragment is read.
+template <int D_, int PF_ = 3>
 struct BfCfg {
-  static constexpr int D = D_, QB = QB_, NW = NW_, WPE = WPE_;
-  static constexpr bool SCHED = SCHED_;   // hand interleaving of QK^T MFMAs and softmax VALU
-  static constexpr int VPM = VPM_;        // VALU instructions per MFMA in that interleave
+  static constexpr int D = D_, PF = PF_;
+  static constexpr int NW = 8;       // waves per workgroup: two groups of one wave per SIMD
 };
 
-constexpr float kLazyLog2 = 8.f;
-
-template <int P> struct Parity { static constexpr int value = P; };
+// A lane whose weights of a tile sum to at most kLazyMax has no weight above
+// it, so the reference maximum only moves when some lane's sum exceeds it.
+// u / l does not depend on the reference, so this is exact up to rounding.
+constexpr float kLazyMax = 256.f;
 
 template <class Cfg, bool CAUSAL, bool PACKED, bool OUT_F32>
-__global__ void __launch_bounds__(Cfg::NW * 64) __attribute__((amdgpu_waves_per_eu(Cfg::WPE)))
+__global__ void __launch_bounds__(Cfg::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 attn_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int D = Cfg::D, QB = Cfg::QB, NW = Cfg::NW;
+  constexpr int D = Cfg::D, NW = Cfg::NW, PF = Cfg::PF;
   constexpr int BN = 64;                 // keys per tile
-  constexpr int QW = 32 * QB;            // query rows per wave
-  constexpr int BM = QW * NW;            // query rows per workgroup
+  constexpr int BM = 32 * NW;            // query rows per workgroup
   constexpr int ROWB = D * 2;            // bytes of one K/V row
   constexpr int TILE = BN * ROWB;        // bytes of one K or V tile
-  constexpr int CPW = TILE / 1024 / NW;  // 1 KB direct-load chunks per wave per tile
+  constexpr int LW = NW / 2;             // waves that issue the tile loads (the second group)
+  constexpr int CPW = TILE / 1024 / LW;  // 1 KB load chunks per loading wave per tile
   constexpr int DC = D / 16;             // k-steps of the QK^T MFMA
   constexpr int DB = D / 32;             // 32-wide blocks of d in O
-  static_assert(CPW * NW * 1024 == TILE, "tile must split into whole 1 KB chunks per wave");
+  constexpr int NQK = 2 * DC;            // QK^T MFMAs per tile and wave
+  constexpr int NPV = 4 * DB;            // P.V MFMAs per tile and wave
+  constexpr int NS = NQK + NPV;          // MFMA steps of a tile
+  static_assert(CPW * LW * 1024 == TILE, "tile must split into whole 1 KB chunks per wave");
+  static_assert(PF >= 1 && PF < NS, "fragment prefetch distance");
 
   // K(j) lives in buffer j % 2, V(j) in buffer 2 + j % 2
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
@@ -89,13 +107,14 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool lag = wave >= NW / 2;       // the second group, one phase behind
   const int hl = lane >> 5;              // which half of the wave
   const int l32 = lane & 31;
   const int q0 = qblk * BM;
-  const int wq0 = q0 + wave * QW;        // first query row of this wave
+  const int wq0 = q0 + wave * 32;        // first query row of this wave
   const int kv_end = CAUSAL ? min(seq_len, q0 + BM) : seq_len;
   const int n_iter = (kv_end + BN - 1) / BN;
-  const int wave_kv_end = CAUSAL ? min(seq_len, wq0 + QW) : seq_len;
+  const int wave_kv_end = CAUSAL ? min(seq_len, wq0 + 32) : seq_len;
   const int wave_iters = (wq0 < seq_len) ? (wave_kv_end + BN - 1) / BN : 0;
 
   const int64_t rs = (int64_t)a.H * D;   // elements between consecutive tokens
@@ -106,54 +125,48 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   const float c = a.c;
 
   // ---- Q fragments (MFMA B operand of S^T = K Q^T), kept for the whole loop
-  bf16x8 qf[QB][DC];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int t = wq0 + qb * 32 + l32;
+  bf16x8 qf[DC];
+  {
+    const int t = wq0 + l32;
     const bool ok = t < seq_len;
     const uint16_t* p = qg + (int64_t)(seq_start + (ok ? t : 0)) * rs + head_off + 8 * hl;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       u32x4 raw = ok ? *(const u32x4*)(p + dc * 16) : (u32x4){0u, 0u, 0u, 0u};
       raw ^= a.qsign;
-      qf[qb][dc] = __builtin_bit_cast(bf16x8, raw);
+      qf[dc] = __builtin_bit_cast(bf16x8, raw);
     }
   }
 
-  // ---- K/V tiles: global -> LDS directly (global_load_lds_dwordx4).  Lane i of
-  // a wave writes LDS bytes [chunk + 16 i, chunk + 16 i + 16); it fetches the
-  // logical granule that the swizzle places there.  The per-lane byte offset
-  // inside a tile is loop-invariant; the tile base is wave-uniform.  Rows past
-  // the end of the sequence re-read its last row: those keys are masked and
-  // their weights are 0.
+  // ---- K/V tiles: HBM -> LDS directly (buffer_load_dwordx4 ... lds).  Lane
+  // i of a wave writes LDS bytes [chunk + 16 i, chunk + 16 i + 16); it fetches
+  // the logical granule that the swizzle places there.  The per-lane byte
+  // offset inside a tile is loop-invariant; the tile base is wave-uniform.  The
+  // buffer's size ends at the end of the sequence, so rows past it read as
+  // zeros (those keys are masked and their weights are 0).
+  const int lw = wave % LW;              // this wave's share of a tile
   uint32_t lane_off[CPW];
-  int lane_row[CPW];
 #pragma unroll
   for (int cc = 0; cc < CPW; ++cc) {
-    const int byte = (wave * CPW + cc) * 1024 + lane * 16;
+    const int byte = (lw * CPW + cc) * 1024 + lane * 16;
     const int row = byte / ROWB;
     const int g = ((byte % ROWB) >> 4) ^ swz<D>(row);
-    lane_row[cc] = row;
     lane_off[cc] = (uint32_t)(((int64_t)row * rs + head_off + g * 8) * 2);
   }
-  auto issue_tile = [&](const uint16_t* __restrict__ src, int buf, int j) {
+  // bytes of one token row of all heads; the host keeps BN rows under 2^32 bytes
+  [[maybe_unused]] const uint32_t row_bytes = (uint32_t)rs * 2u;
+  auto issue_tile = [&](const uint16_t* __restrict__ src, int buf, int j) __attribute__((always_inline)) {
+#if __HIP_DEVICE_COMPILE__   // the 16-byte LDS DMA form exists only for the device target
     const int kv0 = j * BN;
-    const char* base = (const char*)(src + (int64_t)(seq_start + kv0) * rs);
-    char* dst = smem + buf * TILE + wave * CPW * 1024;
-    if (kv0 + BN <= seq_len) {
+    const uint32_t nrec = (uint32_t)min(seq_len - kv0, BN) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)src + (uint64_t)(uint32_t)(seq_start + kv0) * row_bytes), (short)0, (int)nrec,
+        kBufferFlags);
 #pragma unroll
-      for (int cc = 0; cc < CPW; ++cc)
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(base + lane_off[cc]),
-                                         (IAEA_LDS void*)(dst + cc * 1024), 16, 0, 0);
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < CPW; ++cc) {
-        const int over = max(0, kv0 + lane_row[cc] - (seq_len - 1));
-        const uint32_t off = lane_off[cc] - (uint32_t)((int64_t)over * rs * 2);
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(base + off),
-                                         (IAEA_LDS void*)(dst + cc * 1024), 16, 0, 0);
-      }
-    }
+    for (int cc = 0; cc < CPW; ++cc)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (IAEA_LDS void*)(smem + buf * TILE + (lw * CPW + cc) * 1024),
+                                               16, lane_off[cc], 0, 0, 0);
+#endif
   };
 
   // ---- loop-invariant LDS read offsets; buffer bases and the steps over key
@@ -181,162 +194,53 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       }
   }
 
-  auto qk = [&](auto kbuf_tag, f32x16 (&s)[QB][2]) {
-    constexpr int KB = decltype(kbuf_tag)::value;
-    const char* kt = smem + KB * TILE;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 kf = *(const bf16x8*)(kt + kb * 32 * ROWB + koff[dc]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              kf, qf[qb][dc], dc == 0 ? (f32x16){} : s[qb][kb], 0, 0, 0);
-      }
+  // The MFMA steps of the matrix phase of tile j, in issue order.  Steps
+  // [0, NQK) compute S^T(j + 1) = K(j + 1) Q^T, alternating between the two
+  // 32-key halves so consecutive MFMAs are independent; steps [NQK, NS) add
+  // V(j)^T P(j)^T to O^T, 16 keys (chunk kc) at a time.  frag<P, s>() reads
+  // step s's LDS operand for a tile of parity P (K(j + 1) in buffer P ^ 1,
+  // V(j) in buffer 2 + P).
+  auto frag = [&](auto par, auto step) __attribute__((always_inline)) -> bf16x8 {
+    constexpr int P = decltype(par)::value, s = decltype(step)::value;
+    if constexpr (s < NQK) {
+      constexpr int kb = s & 1, dc = s >> 1;
+      return *(const bf16x8*)(smem + (P ^ 1) * TILE + kb * 32 * ROWB + koff[dc]);
+    } else {
+      constexpr int kc = (s - NQK) / DB, db = (s - NQK) % DB;
+      const char* vt = smem + (2 + P) * TILE + kc * 16 * ROWB;
+      const bf16x4 lo = ds_read_tr16(vt + voff[0][db]);
+      const bf16x4 hi = ds_read_tr16(vt + voff[1][db]);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
 
-  f32x16 oacc[QB][DB];
-  float m_run[QB], l_run[QB], lx_run[QB];   // reference max, rounded and exact sums
+  // ---- running state
+  // m_run: reference maximum of the row (raw score units); lx_run: this lane's
+  // sum of the weights (half of the row's keys); oacc: u^T; lacc: l, the sum of
+  // the bf16-rounded weights that enter P.V (see the row-sum MFMA below).
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-    lx_run[qb] = 0.f;
+  for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
+  float m_run = -INFINITY, lx_run = 0.f;
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+  f32x16 negm;                           // -m_run in every register: the score MFMA's start value
+  f32x16 sc[2];                          // S^T of the current tile (two 32-key halves)
+  bf16x8 pf[4];                          // P^T of the current tile, four 16-key chunks
+
+  // The row sums come from v_mfma_f32_16x16x32_bf16 with a 0/1 selector as
+  // the A operand: in a P fragment lanes n and n + 32 hold query n and lanes
+  // n + 16 and n + 48 query n + 16, so rows 0-7 of the selector pick k-groups
+  // 0 and 2 and rows 8-15 k-groups 1 and 3.  Result lane i then holds query i
+  // (i < 16), i - 16 (16 <= i < 48) or i - 32 (i >= 48).
+  bf16x8 lsel;
+  {
+    const __bf16 one = ((lane & 15) < 8) == (((lane >> 4) & 1) == 0) ? (__bf16)1.0f : (__bf16)0.0f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[qb][db] = (f32x16){};
+    for (int jj = 0; jj < 8; ++jj) lsel[jj] = one;
   }
+  const int lacc_query_lane = (lane >= 16 && lane < 48) ? lane - 16 : lane;
 
-  // P = exp2(s * c - ms) for one 32-query block, rounded to bf16 and packed as
-  // the four 16-key B operands of O^T += V^T P^T.  Also returns this lane's
-  // sums of the weights: lr of the bf16-rounded ones (those enter P.V, so
-  // u / lr is an exact weighted average of them: a dominant key returns its
-  // value) and lx of the unrounded ones (for the LSE).
-  auto weights = [&](const f32x16 (&sq)[2], float ms, bf16x8 (&pq)[4], float& lr, float& lx) {
-    float r0 = 0.f, r1 = 0.f, x0 = 0.f, x1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(__builtin_fmaf(sq[kb][8 * c2 + 2 * j], c, -ms));
-          const float p1 = fast_exp2(__builtin_fmaf(sq[kb][8 * c2 + 2 * j + 1], c, -ms));
-          const uint32_t pk = pack_bf16x2(p0, p1);
-          if (j & 1) { r1 = sum2_bf16(pk, r1); x1 += p0 + p1; }
-          else       { r0 = sum2_bf16(pk, r0); x0 += p0 + p1; }
-          w[j] = pk;
-        }
-        pq[kb * 2 + c2] = __builtin_bit_cast(bf16x8, w);
-      }
-    lr = r0 + r1;
-    lx = x0 + x1;
-  };
-
-  // one pipeline step for tile `it` (parity P): S(it) is in s_cur; S(it + 1)
-  // goes to s_nxt on the matrix cores while S(it)'s softmax runs on the VALU
-  auto step = [&](auto par, int it, f32x16 (&s_cur)[QB][2], f32x16 (&s_nxt)[QB][2]) {
-    constexpr int P = decltype(par)::value;
-    // prefetch K two tiles ahead into the buffer K(it) used, V one tile ahead
-    if (it + 2 < n_iter) issue_tile(kg, P, it + 2);
-    if (it + 1 < n_iter) issue_tile(vg, 2 + (P ^ 1), it + 1);
-
-    if (it < wave_iters) {
-      const int kv0 = it * BN;
-      // mask keys past the end of the sequence and, when causal, future keys:
-      // the key of register r is kv0 + kb*32 + (r/4)*8 + half*4 + r%4
-      const bool edge = (kv0 + BN > seq_len) || (CAUSAL && kv0 + BN - 1 > wq0);
-      if (edge) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int lim = (CAUSAL ? min(wq0 + qb * 32 + l32, seq_len - 1) : seq_len - 1) - (kv0 + hl * 4);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) s_cur[qb][kb][r] = -INFINITY;
-        }
-      }
-
-      // unconditional, so the matrix work shares a basic block with the
-      // softmax below and the two can be interleaved; past the wave's last
-      // tile the result is never used
-      qk(Parity<P ^ 1>{}, s_nxt);
-
-      // running-statistics softmax update of this tile.  The weights are first
-      // formed against the current reference maximum m (no dependence on this
-      // tile's maximum, so they overlap the MFMAs above).  The reference moves
-      // to m_new = max(m, m_b) - and the old l and u are scaled by
-      // exp(m - m_new) - only when some row of the wave grew by more than
-      // 2^kLazyLog2 (always on a row's first tile, where m = -inf); then the
-      // weights are formed again.  u / l does not depend on the reference.
-      bf16x8 pf[QB][4];
-      float mx[QB], lr[QB], lx[QB];
-      bool move = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float ms = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
-        weights(s_cur[qb], ms, pf[qb], lr[qb], lx[qb]);
-        float m = fmaxf(s_cur[qb][0][0], s_cur[qb][1][0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) m = fmaxf(m, fmaxf(s_cur[qb][0][r], s_cur[qb][1][r]));
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
-                                                         false, false);
-        mx[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        move |= (mx[qb] - m_run[qb]) * c > kLazyLog2 || m_run[qb] == -INFINITY;
-      }
-      if constexpr (Cfg::SCHED) {
-        // interleave: one K-fragment read, one MFMA of S(it + 1), then a slice
-        // of this tile's softmax, so the VALU runs under the matrix cores
-#pragma unroll
-        for (int i = 0; i < 2 * DC * QB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, Cfg::VPM, 0);   // VALU
-        }
-      }
-      if (__ballot(move) != 0) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float m_new = fmaxf(m_run[qb], mx[qb]);
-          const float alpha = (m_run[qb] == -INFINITY) ? 0.f : fast_exp2((m_run[qb] - m_new) * c);
-          m_run[qb] = m_new;
-          l_run[qb] *= alpha;
-          lx_run[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
-          const float ms = (m_new == -INFINITY) ? 0.f : m_new * c;
-          weights(s_cur[qb], ms, pf[qb], lr[qb], lx[qb]);
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        l_run[qb] += lr[qb];
-        lx_run[qb] += lx[qb];
-      }
-
-      // O^T += V^T P^T over four 16-key chunks
-      const char* vt = smem + (2 + P) * TILE;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x4 lo = ds_read_tr16(vt + kc * 16 * ROWB + voff[0][db]);
-          const bf16x4 hi = ds_read_tr16(vt + kc * 16 * ROWB + voff[1][db]);
-          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kc], oacc[qb][db], 0, 0, 0);
-        }
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-
-  // prologue: K(0), K(1), V(0) resident, S(0) computed
+  // ---- prologue: K(0), K(1), V(0) resident, S(0) computed from 0 (every wave)
   if (n_iter > 0) {
     issue_tile(kg, 0, 0);
     issue_tile(vg, 2, 0);
@@ -344,38 +248,179 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  f32x16 sa[QB][2], sb[QB][2];
-  if (wave_iters > 0) qk(Parity<0>{}, sa);
+  if (wave_iters > 0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 kf = *(const bf16x8*)(smem + kb * 32 * ROWB + koff[dc]);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[dc], dc == 0 ? (f32x16){} : sc[kb], 0, 0, 0);
+      }
+  }
   __syncthreads();   // every wave has read K(0) before K(2) replaces it
 
-  for (int it = 0; it < n_iter; it += 2) {
-    step(Parity<0>{}, it, sa, sb);
-    if (it + 1 < n_iter) step(Parity<1>{}, it + 1, sb, sa);
-  }
-
-  // ---- epilogue: O = u / l, LSE = ln2 * (m * c + log2 l)
-  const int64_t lse_base = PACKED ? ((int64_t)h * a.N + seq_start) : ((int64_t)(b * a.H + h) * a.N);
+  // Weights exp2(s' c - shift_c) of the tile into pf, where s' = s - m_run
+  // (the score MFMAs start from -m_run); returns this lane's sum of them.
+  auto weights = [&](float shift_c, bool fused) __attribute__((always_inline)) -> float {
+    float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[qb]),
-                                                     __float_as_uint(l_run[qb]), false, false);
-    const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const auto swx = __builtin_amdgcn_permlane32_swap(__float_as_uint(lx_run[qb]),
-                                                      __float_as_uint(lx_run[qb]), false, false);
-    const float lx_tot = __uint_as_float(swx[0]) + __uint_as_float(swx[1]);
-    const int t = wq0 + qb * 32 + l32;
-    if (t >= seq_len) continue;
+    for (int ch = 0; ch < 4; ++ch) {
+      // registers 8 c2 .. 8 c2 + 7 of the kb half: keys of chunk ch
+      const int kb = ch / 2, c2 = ch % 2;
+      u32x4 w;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float s0 = sc[kb][8 * c2 + 2 * jj], s1 = sc[kb][8 * c2 + 2 * jj + 1];
+        const float e0 = fast_exp2(fused ? __builtin_fmaf(s0, c, -shift_c) : s0 * c);
+        const float e1 = fast_exp2(fused ? __builtin_fmaf(s1, c, -shift_c) : s1 * c);
+        w[jj] = pack_bf16x2(e0, e1);
+        if (jj & 1) x1 += e0 + e1;
+        else        x0 += e0 + e1;
+      }
+      pf[ch] = __builtin_bit_cast(bf16x8, w);
+    }
+    return x0 + x1;
+  };
+
+  // Softmax phase Y(j).  The score MFMAs start from -m, so tile j arrives as
+  // s - m and its weight is exp2((s - m) c) with one multiply; the tile's row
+  // maximum is not needed to form the weights.  Only when some lane's weights
+  // sum to more than kLazyMax (and on a row's first tile, whose scores were
+  // computed from 0) does the wave take the maximum, move the reference to it,
+  // scale the running state by exp(m - m_new) and form the weights again -
+  // before P(j) enters P.V in X(j).  The second group issues the loads of
+  // K(j + 2) and V(j + 1) here, where they share issue slots with VALU work.
+  auto phase_y = [&](auto par, int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    if (lag) {
+      if (j + 2 < n_iter) issue_tile(kg, P, j + 2);          // into the buffer of K(j)
+      if (j + 1 < n_iter) issue_tile(vg, 2 + (P ^ 1), j + 1);  // into the buffer of V(j - 1)
+    }
+    if (j < wave_iters) {
+      const int kv0 = j * BN;
+      // keys past the end of the sequence and, when causal, future keys get
+      // -inf; the key of register r is kv0 + kb*32 + (r/4)*8 + half*4 + r%4
+      if ((kv0 + BN > seq_len) || (CAUSAL && kv0 + BN - 1 > wq0)) {
+        const int lim = (CAUSAL ? min(wq0 + l32, seq_len - 1) : seq_len - 1) - (kv0 + hl * 4);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) sc[kb][r] = -INFINITY;
+      }
+      float lx = weights(0.f, false);
+      const bool first = m_run == -INFINITY;
+      if (__ballot(lx > kLazyMax || first) != 0) {
+        float m = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, fmaxf(sc[0][r], sc[1][r]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        if (first) {
+          // S(0) was computed from 0: the reference becomes the row maximum
+          m_run = mx;
+          lx = weights(mx * c, true);
+        } else {
+          // scores are relative to m_run.  The reference moves by a whole
+          // number k of exp2 units, so the running state scales by exactly
+          // 2^-k, and so do this tile's bf16 weights: k comes off their
+          // exponent fields (a weight that would drop below the smallest
+          // bf16 becomes 0).  Weights that may have overflowed (k >= 120) are
+          // formed again instead.
+          const float kf = fminf(ceilf(fmaxf(mx, 0.f) * c), 200.f);
+          const float alpha = __builtin_amdgcn_ldexpf(1.f, -(int)kf);
+          m_run += kf / c;
+          lx_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          lacc *= __shfl(alpha, lacc_query_lane);
+          if (__ballot(kf >= 120.f) != 0) {
+            lx = weights(kf, true);
+          } else {
+            const unsigned short dk = (unsigned short)((int)kf << 7);
+            const u16x8 dk8 = {dk, dk, dk, dk, dk, dk, dk, dk};
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch)
+              pf[ch] = __builtin_bit_cast(bf16x8, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x8, pf[ch]), dk8));
+            lx *= alpha;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) negm[r] = -m_run;
+      }
+      lx_run += lx;
+    }
+    __syncthreads();
+  };
+
+  // Matrix phase X(j): S(j + 1) into sc, O^T += V(j)^T P(j)^T, l += row sums
+  // of P(j).  MFMAs and LDS reads only; operand fragments are read PF steps
+  // ahead of their MFMA.  The second group waits here for the tile loads it
+  // issued in Y(j).
+  auto phase_x = [&](auto par, int j) __attribute__((always_inline)) {
+    if (j < wave_iters) {
+      bf16x8 fr[PF + 1];
+      static_for<PF>([&](auto step) __attribute__((always_inline)) {
+        fr[decltype(step)::value] = frag(par, step);
+      });
+      static_for<NS>([&](auto step) __attribute__((always_inline)) {
+        constexpr int s = decltype(step)::value;
+        if constexpr (s + PF < NS) fr[(s + PF) % (PF + 1)] = frag(par, std::integral_constant<int, s + PF>{});
+        if constexpr (s < NQK) {
+          constexpr int kb = s & 1, dc = s >> 1;
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s % (PF + 1)], qf[dc],
+                                                           dc == 0 ? negm : sc[kb], 0, 0, 0);
+        } else {
+          constexpr int kc = (s - NQK) / DB, db = (s - NQK) % DB;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s % (PF + 1)], pf[kc], oacc[db], 0, 0, 0);
+          if constexpr (db == DB - 1)
+            lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pf[kc], lacc, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    if (lag) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  // Phase schedule.  The first group runs Y(0) X(0) Y(1) X(1) ...; the second
+  // group runs the same one phase later.  In the phase where the first group
+  // runs X(j) the second runs Y(j) and issues K(j + 2) and V(j + 1); their
+  // buffers held K(j) and V(j - 1), last read in the phase before (X(j - 1)
+  // of the second group).  They are waited for at the end of the second
+  // group's X(j), one phase before the first group's X(j + 1) reads them.
+  if (lag) __syncthreads();
+  for (int j = 0; j < n_iter; j += 2) {
+    phase_y(Parity<0>{}, j);
+    phase_x(Parity<0>{}, j);
+    if (j + 1 < n_iter) {
+      phase_y(Parity<1>{}, j + 1);
+      phase_x(Parity<1>{}, j + 1);
+    }
+  }
+  if (!lag) __syncthreads();
+
+  // ---- epilogue: O = u / l, LSE = ln2 * (m * c + log2 lx)
+  // l of this lane's query i % 32 sits in lacc of lane i + 16 (16 <= i < 32),
+  // i - 32 (32 <= i < 48) or i itself
+  const int lsrc = (lane >= 16 && lane < 32) ? lane + 16 : (lane >= 32 && lane < 48) ? lane - 32 : lane;
+  const float l_tot = __shfl(lacc[0], lsrc);
+  const auto swx = __builtin_amdgcn_permlane32_swap(__float_as_uint(lx_run), __float_as_uint(lx_run), false, false);
+  const float lx_tot = __uint_as_float(swx[0]) + __uint_as_float(swx[1]);
+  const int64_t lse_base = PACKED ? ((int64_t)h * a.N + seq_start) : ((int64_t)(b * a.H + h) * a.N);
+  const int t = wq0 + l32;
+  if (t < seq_len) {
     const bool any = l_tot > 0.f;
     const float inv = any ? 1.f / l_tot : 0.f;
-    if (hl == 0) a.lse[lse_base + t] = any ? kLn2 * (m_run[qb] * c + __log2f(lx_tot)) : -INFINITY;
+    if (hl == 0) a.lse[lse_base + t] = any ? kLn2 * (m_run * c + __log2f(lx_tot)) : -INFINITY;
     const int64_t orow = (int64_t)(seq_start + t) * rs + head_off;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db * 32 + g * 8 + hl * 4;
-        const float o0 = oacc[qb][db][g * 4 + 0] * inv, o1 = oacc[qb][db][g * 4 + 1] * inv;
-        const float o2 = oacc[qb][db][g * 4 + 2] * inv, o3 = oacc[qb][db][g * 4 + 3] * inv;
+        const float o0 = oacc[db][g * 4 + 0] * inv, o1 = oacc[db][g * 4 + 1] * inv;
+        const float o2 = oacc[db][g * 4 + 2] * inv, o3 = oacc[db][g * 4 + 3] * inv;
         if constexpr (OUT_F32) {
           *(f32x4*)((float*)a.o + orow + d) = (f32x4){o0, o1, o2, o3};
         } else {
@@ -392,7 +437,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 template <class Cfg, bool CAUSAL, bool PACKED, bool OUT_F32>
 static hipError_t launch_one(FwdArgs a, hipStream_t st) {
   constexpr int NW = Cfg::NW;
-  constexpr int BM = 32 * Cfg::QB * NW;
+  constexpr int BM = 32 * NW;
   if (PACKED) {
     a.slots = (a.N + BM - 1) / BM + a.B;
     a.n_work = a.H * a.slots;
@@ -409,9 +454,7 @@ static hipError_t launch_one(FwdArgs a, hipStream_t st) {
 }
 
 // Kernel instance per head dimension.
-template <int D> struct BfTile;
-template <> struct BfTile<128> { using Cfg = BfCfg<128, 1, 4, 2, false>; };
-template <> struct BfTile<64>  { using Cfg = BfCfg<64, 1, 4, 2, false>; };
+template <int D> struct BfTile { using Cfg = BfCfg<D, 3>; };
 
 template <int D, bool CAUSAL, bool PACKED>
 static hipError_t launch_d(const FwdArgs& a, bool out_f32, hipStream_t st) {
@@ -431,9 +474,7 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, int d, bool causal, bool packe
 }
 
 int bf16_rows_per_workgroup(int d) {
-  using C128 = BfTile<128>::Cfg;
-  using C64 = BfTile<64>::Cfg;
-  return d == 128 ? 32 * C128::QB * C128::NW : 32 * C64::QB * C64::NW;
+  return d == 128 ? 32 * BfTile<128>::Cfg::NW : 32 * BfTile<64>::Cfg::NW;
 }
 
 }  // namespace iaea

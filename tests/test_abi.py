@@ -65,6 +65,7 @@ def fp8(**kw):
     (dict(q=MIS), ia.ATTN_ERR_ALIGN), (dict(o=MIS), ia.ATTN_ERR_ALIGN), (dict(lse=MIS), ia.ATTN_ERR_ALIGN),
     (dict(cu_seqlens=MIS), ia.ATTN_ERR_ALIGN),
     (dict(cu_seqlens=P, B=1 << 30, H=4, N=1 << 0), ia.ATTN_ERR_SHAPE),
+    (dict(H=(1 << 17) + 1, N=1), ia.ATTN_ERR_SHAPE),     # H * d > 2^24
 ])
 def test_attn_fwd_rejects(kw, status):
     assert bf16(**kw) == status
