@@ -40,6 +40,31 @@ def flops(w, lengths=None):
     return f / 2 if w.causal else f
 
 
+def exact_pair_flops(w, lengths=None):
+    """4 d flops per visible (query, key) pair, counting the causal diagonal
+    exactly (N (N + 1) / 2 pairs per sequence instead of N^2 / 2)."""
+    def per_seq(L):
+        return 4.0 * w.d * (L * (L + 1) / 2 if w.causal else float(L) * L)
+    if w.varlen:
+        return float(sum(w.H * per_seq(int(L)) for L in lengths))
+    return w.B * w.H * per_seq(w.N)
+
+
+def tile_flops(w, lengths=None, rows=32, keys=64):
+    """MFMA work the kernels actually do: every wave owns `rows` query rows
+    and multiplies whole `keys`-key tiles up to the last key any of its rows
+    may see, so diagonal and ragged tiles are computed in full."""
+    def per_seq(L):
+        tiles = 0
+        for r0 in range(0, L, rows):
+            last = min(L, r0 + rows) if w.causal else L
+            tiles += -(-last // keys)
+        return 4.0 * w.d * rows * keys * tiles
+    if w.varlen:
+        return float(sum(w.H * per_seq(int(L)) for L in lengths))
+    return w.B * w.H * per_seq(w.N)
+
+
 def algorithmic_bytes(w):
     """Q, K, V read once plus O and LSE written once."""
     tokens = w.N if w.varlen else w.B * w.N
@@ -57,17 +82,19 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(wname):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    counters, valid only while the kernel sources are unchanged."""
+def counters_from_profiles(wname):
+    """HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE) and the shader
+    clock under load (GRBM_GUI_ACTIVE over the kernel's duration) from the
+    committed counter summaries, valid only while the kernel sources are
+    unchanged."""
     p = os.path.join(ROOT, "profiles", f"traffic_{wname}.json")
     if not os.path.exists(p):
-        return None
+        return {}
     with open(p, encoding="utf-8") as f:
         t = json.load(f)
     if t.get("source_hash") != source_hash():
-        return None
-    return t.get("bytes_per_launch")
+        return {}
+    return t
 
 
 def cpu_baseline(w, inp, O_gpu, budget_s):
@@ -116,6 +143,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="size of the scratch write that evicts the caches before each launch "
+                         "of the cache-cold timing pass (0 skips that pass)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB (the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -214,10 +244,29 @@ def main():
         b_.synchronize()
         per.append(a_.elapsed_time(b_))
 
+    # cache-cold pass: a scratch write of --flush-mib MiB between launches
+    # evicts L2 and the Infinity Cache; only the launch is timed
+    cold = []
+    if args.flush_mib > 0:
+        scratch = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        for i in range(5):
+            scratch.fill_(float(i))
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            step()
+            b_.record(stream)
+            b_.synchronize()
+            cold.append(a_.elapsed_time(b_))
+        del scratch
+
     F = flops(w, inp.get("lengths"))
+    F_pairs = exact_pair_flops(w, inp.get("lengths"))
+    F_tiles = tile_flops(w, inp.get("lengths"))
     tflops = F / (ms * 1e-3) / 1e12
     peak = PEAK[dtype]
-    traffic = traffic_from_profiles(w.name)
+    counters = counters_from_profiles(w.name)
+    traffic = counters.get("bytes_per_launch")
+    clk = counters.get("clock_ghz")
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -233,14 +282,23 @@ def main():
         "data": "synthetic (seeded numpy PCG64 inputs of the workload's shape and distribution)",
         "config": {"workload": w.name, "B": B, "H": w.H, "N": N, "d": w.d, "causal": w.causal,
                    "packed": w.varlen, "out": w.out, "scale": w.scale, "flop_per_step": F,
-                   "kernel": kname},
+                   "flop_per_step_exact_pairs": F_pairs, "flop_per_step_computed_tiles": F_tiles,
+                   "tile_efficiency": round(F_pairs / F_tiles, 4), "kernel": kname},
         "pct_of_peak": round(100 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic,
-                     "algorithmic_bytes": algorithmic_bytes(w)},
+                     "algorithmic_bytes": algorithmic_bytes(w),
+                     # the published peak assumes 2.4 GHz; under this load the
+                     # shader clock runs lower, which caps the attainable rate
+                     "clock_ghz_measured": clk,
+                     "peak_at_measured_clock": round(peak * clk / 2.4, 1) if clk else None,
+                     "frac_at_measured_clock": round(tflops / (peak * clk / 2.4), 4) if clk else None},
         "timing": {"first_launch_ms": round(first_ms, 3), "wall_ms_timed_region": round(wall_ms, 3),
                    "per_launch_ms_min": round(min(per), 5), "per_launch_ms_median": round(float(np.median(per)), 5),
-                   "per_launch_ms_max": round(max(per), 5)},
+                   "per_launch_ms_max": round(max(per), 5),
+                   "cache_cold_flush_mib": args.flush_mib,
+                   "cache_cold_ms_median": round(float(np.median(cold)), 5) if cold else None,
+                   "cache_cold_tflops": round(F / (float(np.median(cold)) * 1e-3) / 1e12, 2) if cold else None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
