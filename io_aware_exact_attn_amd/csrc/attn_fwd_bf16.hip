@@ -75,9 +75,12 @@ struct BfCfg {
 };
 
 // A lane whose weights of a tile sum to at most kLazyMax has no weight above
-// it, so the reference maximum only moves when some lane's sum exceeds it.
-// u / l does not depend on the reference, so this is exact up to rounding.
-constexpr float kLazyMax = 256.f;
+// it, so the reference maximum only moves when some lane's sum exceeds it (or
+// a weight overflows to inf).  u / l does not depend on the reference, so this
+// is exact up to rounding; bf16 and fp32 keep the same relative precision at
+// any magnitude.  The bound only limits range: with weights <= 2^64 the fp32
+// sums l and u stay finite while N * max|v| stays below 2^68.
+constexpr float kLazyMax = 0x1p64;
 
 template <class Cfg, bool CAUSAL, bool PACKED, bool OUT_F32>
 __global__ void __launch_bounds__(Cfg::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -162,10 +165,15 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const char*)src + (uint64_t)(uint32_t)(seq_start + kv0) * row_bytes), (short)0, (int)nrec,
         kBufferFlags);
-#pragma unroll
-    for (int cc = 0; cc < CPW; ++cc)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (IAEA_LDS void*)(smem + buf * TILE + (lw * CPW + cc) * 1024),
-                                               16, lane_off[cc], 0, 0, 0);
+    // one LDS base (M0) for all chunks: chunk cc's 1 KB step rides in the
+    // instruction offset, which applies to the LDS and the memory address
+    // alike, so the memory offset gives it back (lane_off[cc] >= cc * 1 KB,
+    // since a token row in memory is at least as long as one in the tile)
+    static_for<CPW>([&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (IAEA_LDS void*)(smem + buf * TILE + lw * CPW * 1024),
+                                               16, lane_off[cc] - cc * 1024, 0, cc * 1024, 0);
+    });
 #endif
   };
 
@@ -238,7 +246,8 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) lsel[jj] = one;
   }
-  const int lacc_query_lane = (lane >= 16 && lane < 48) ? lane - 16 : lane;
+  const bool lacc_swapped = lane >= 16 && lane < 48;
+  const float inv_c = 1.f / c;
 
   // ---- prologue: K(0), K(1), V(0) resident, S(0) computed from 0 (every wave)
   if (n_iter > 0) {
@@ -321,22 +330,24 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           m_run = mx;
           lx = weights(mx * c, true);
         } else {
-          // scores are relative to m_run.  The reference moves by a whole
-          // number k of exp2 units, so the running state scales by exactly
-          // 2^-k, and so do this tile's bf16 weights: k comes off their
-          // exponent fields (a weight that would drop below the smallest
-          // bf16 becomes 0).  Weights that may have overflowed (k >= 120) are
-          // formed again instead.
-          const float kf = fminf(ceilf(fmaxf(mx, 0.f) * c), 200.f);
-          const float alpha = __builtin_amdgcn_ldexpf(1.f, -(int)kf);
-          m_run += kf / c;
-          lx_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-          lacc *= __shfl(alpha, lacc_query_lane);
-          if (__ballot(kf >= 120.f) != 0) {
-            lx = weights(kf, true);
+          // scores are relative to m_run; this lane's reference moves up by
+          // mc = max(mx, 0) c exp2 units
+          const float mc = fmaxf(mx, 0.f) * c;
+          float alpha;
+          if (__ballot(mc > 119.f) != 0) {
+            // a large move, whose weights may have overflowed: shift by
+            // exactly mc and form them again
+            alpha = fast_exp2(-mc);
+            m_run += fmaxf(mx, 0.f);
+            lx = weights(mc, true);
           } else {
+            // a small move by a whole number k of exp2 units: the running
+            // state scales by exactly 2^-k, and so do this tile's bf16
+            // weights, k coming off their exponent fields (a weight that
+            // would drop below the smallest normal bf16 becomes 0)
+            const float kf = ceilf(mc);
+            alpha = __builtin_amdgcn_ldexpf(1.f, -(int)kf);
+            m_run = __builtin_fmaf(kf, inv_c, m_run);
             const unsigned short dk = (unsigned short)((int)kf << 7);
             const u16x8 dk8 = {dk, dk, dk, dk, dk, dk, dk, dk};
 #pragma unroll
@@ -344,13 +355,26 @@ attn_fwd_bf16_kernel(FwdArgs a) {
               pf[ch] = __builtin_bit_cast(bf16x8, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x8, pf[ch]), dk8));
             lx *= alpha;
           }
+          lx_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          // lacc lane i holds the query of lane i ^ 16 for 16 <= i < 48 (its
+          // own otherwise); the 16-lane swap hands every lane the alpha of
+          // lane i ^ 16 as one of its two results, the one that is not its own
+          const auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha),
+                                                            false, false);
+          const float partner = __uint_as_float(a16[0] == __float_as_uint(alpha) ? a16[1] : a16[0]);
+          lacc *= lacc_swapped ? partner : alpha;
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) negm[r] = -m_run;
       }
       lx_run += lx;
     }
-    __syncthreads();
+    // a bare s_barrier: __syncthreads() would also wait here for the tile
+    // loads just issued, which are waited for at the end of X(j) instead.
+    // The memory clobber keeps LDS accesses on their side of it.
+    asm volatile("s_barrier" ::: "memory");
   };
 
   // Matrix phase X(j): S(j + 1) into sc, O^T += V(j)^T P(j)^T, l += row sums

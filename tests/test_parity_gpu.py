@@ -104,6 +104,30 @@ def test_large_scores_qk_outliers(causal, out):
     _check(q, k, v, 1 / math.sqrt(128), causal, out)
 
 
+@pytest.mark.parametrize("per_tile,N,d", [(80.0, 300, 128), (170.0, 200, 128), (400.0, 136, 128),
+                                           (170.0, 200, 64)])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_rising_scores(per_tile, N, d, causal):
+    """Scores that rise along the keys by about `per_tile` exp2 units per
+    64-key tile move every row's reference maximum on nearly every tile: by
+    fewer than 120 units (the kernel rescales the weights it formed in place)
+    or by more (it forms them again; at 400 units they overflow fp32 before
+    the shift).  Magnitudes stay where fp32 scores are accurate to ~1e-4 in
+    the exponent, so the workload tolerances apply."""
+    scale = 1 / math.sqrt(d)
+    c = scale / math.log(2.0)
+    slope = per_tile / (64 * 4.0 * c)          # q[..., 0] = 4: 4 * slope raw score per key
+    rng = np.random.default_rng(int(per_tile) * 1000 + N + d)
+    q = rng.standard_normal((1, N, 2, d)).astype(np.float32) * np.float32(0.05)
+    q[..., 0] = 4.0
+    k = rng.standard_normal((1, N, 2, d)).astype(np.float32)
+    k[..., 0] = (np.float32(slope) * np.arange(N, dtype=np.float32))[None, :, None]
+    v = rng.standard_normal((1, N, 2, d)).astype(np.float32)
+    q, k, v = (W.f32_to_bf16_bits(x) for x in (q, k, v))
+    for out in ("bf16", "f32"):
+        _check(q, k, v, scale, causal, out)
+
+
 def test_value_outliers_bound():
     """With +-20 outliers in V as well, the bf16 rounding of P before the P.V
     contraction bounds the error by u * max|v| (u = 2^-8, the unit roundoff
