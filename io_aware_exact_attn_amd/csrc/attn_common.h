@@ -50,7 +50,8 @@ struct FwdArgs {
 };
 
 // Undo the round-robin XCD dispatch: consecutive logical indices land on one
-// XCD, so workgroups that run together on an XCD share its L2.
+// XCD, so workgroups that run together on an XCD share its L2 (packed
+// documents: a head's documents stay together).
 __device__ __forceinline__ int logical_block(int bid, int per_xcd) {
   return (bid % kXcds) * per_xcd + bid / kXcds;
 }
@@ -64,16 +65,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Locate (head, sequence start, length, q block) of this workgroup.  Returns
+// Locate (head, sequence start, length, q block) of workgroup bid.  Returns
 // false when the workgroup has no work (grid padding, or packed slots past the
 // last document).
+//
+// Fixed-length sequences: the workgroups go out in rank order of their cost
+// (rank r covers q block slots - 1 - r of every (sequence, head) when causal),
+// so the dispatcher, which hands the next workgroup to the first free CU,
+// schedules longest first and the last ones to start are the shortest.  The
+// (sequence, head) index is the minor one: the round-robin over the 8 XCDs
+// then keeps each (sequence, head) on one XCD when B H is a multiple of 8.
 template <int BM, bool CAUSAL, bool PACKED>
-__device__ __forceinline__ bool decode_work(const FwdArgs& a, int lb, int& h, int& b,
+__device__ __forceinline__ bool decode_work(const FwdArgs& a, int bid, int& h, int& b,
                                             int& seq_start, int& seq_len, int& qblk) {
-  if (lb >= a.n_work) return false;
   if constexpr (!PACKED) {
-    const int bh = lb / a.slots;
-    const int r = lb - bh * a.slots;
+    const int lb = bid;
+    if (lb >= a.n_work) return false;
+    const int nbh = a.B * a.H;
+    const int r = lb / nbh;
+    const int bh = lb - r * nbh;
     qblk = CAUSAL ? (a.slots - 1 - r) : r;
     b = bh / a.H;
     h = bh - b * a.H;
@@ -81,6 +91,8 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, int lb, int& h, in
     seq_len = a.N;
     return true;
   } else {
+    const int lb = logical_block(bid, a.per_xcd);
+    if (lb >= a.n_work) return false;
     h = lb / a.slots;
     const int s = lb - h * a.slots;
     b = 0;

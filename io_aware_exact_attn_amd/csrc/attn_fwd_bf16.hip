@@ -29,8 +29,9 @@
 //  * LDS rows are XOR-swizzled in 16-byte granules so both the K fragment
 //    reads and the transposed V reads are free of bank conflicts.
 //  * Causal: tiles above the diagonal are never loaded or computed, and
-//    workgroups are issued heaviest first; the block -> tile mapping keeps
-//    the workgroups of one head on one XCD (L2) at a time.
+//    workgroups are issued longest first across all heads (the dispatcher
+//    then balances the CUs like a longest-first list schedule), with each
+//    head kept on one XCD (L2).
 #include "attn_common.h"
 #include "attn_kernels.h"
 
@@ -104,7 +105,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
 
   int h, b, seq_start, seq_len, qblk;
-  if (!decode_work<BM, CAUSAL, PACKED>(a, logical_block(blockIdx.x, a.per_xcd), h, b,
+  if (!decode_work<BM, CAUSAL, PACKED>(a, blockIdx.x, h, b,
                                        seq_start, seq_len, qblk))
     return;
 
@@ -133,9 +134,13 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     const int t = wq0 + l32;
     const bool ok = t < seq_len;
     const uint16_t* p = qg + (int64_t)(seq_start + (ok ? t : 0)) * rs + head_off + 8 * hl;
+    // rows past the end read row 0 and are zeroed: the loads stay
+    // unconditional, so they issue together with the tile loads below
+    const uint32_t keep = ok ? 0xffffffffu : 0u;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
-      u32x4 raw = ok ? *(const u32x4*)(p + dc * 16) : (u32x4){0u, 0u, 0u, 0u};
+      u32x4 raw = *(const u32x4*)(p + dc * 16);
+      raw &= keep;
       raw ^= a.qsign;
       qf[dc] = __builtin_bit_cast(bf16x8, raw);
     }

@@ -95,7 +95,7 @@ attn_fwd_fp8_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
 
   int h, b, seq_start, seq_len, qblk;
-  if (!decode_work<BM, CAUSAL, false>(a, logical_block(blockIdx.x, a.per_xcd), h, b,
+  if (!decode_work<BM, CAUSAL, false>(a, blockIdx.x, h, b,
                                       seq_start, seq_len, qblk))
     return;
 
