@@ -128,8 +128,10 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  *   maximum is subtracted, so no data-dependent scale is needed; a data-
  *   dependent one would read future keys).  P is carried as two e4m3 terms
  *   (P ~ hi + lo, hi = e4m3(P * 2^8) / 2^8, lo = e4m3((P - hi) * 2^12) / 2^12);
- *   the normaliser l is summed from the unquantised fp32 P.
- *   Other arguments as attn_fwd; cu_seqlens must be NULL.
+ *   the normaliser l is summed from the unquantised fp32 P.  Scales must be
+ *   positive, finite and normal.
+ *   Other arguments as attn_fwd; cu_seqlens must be NULL.  H * d must not
+ *   exceed 2^24 (ATTN_ERR_SHAPE).
  */
 ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
                           const float* q_scale, const float* k_scale, const float* v_scale,

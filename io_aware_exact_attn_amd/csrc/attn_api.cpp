@@ -78,6 +78,8 @@ ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
   if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_NULL;
   if (d != 128) return ATTN_ERR_UNSUPPORTED;
   if (cu_seqlens) return ATTN_ERR_UNSUPPORTED;
+  // a 64-row K/V tile of all heads (64 * H * d bytes) is addressed with 32-bit offsets
+  if ((int64_t)H * d > ((int64_t)1 << 24)) return ATTN_ERR_SHAPE;
   if (!aligned16(q_scale) || !aligned16(k_scale) || !aligned16(v_scale)) return ATTN_ERR_ALIGN;
   a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
   a.nsb = (N + 127) / 128;

@@ -79,6 +79,7 @@ def test_attn_fwd_rejects(kw, status):
     (dict(scale=float("-inf")), ia.ATTN_ERR_SCALE),
     (dict(k_scale=MIS), ia.ATTN_ERR_ALIGN), (dict(v=MIS), ia.ATTN_ERR_ALIGN),
     (dict(N=0), ia.ATTN_ERR_SHAPE),
+    (dict(H=(1 << 17) + 1, N=1), ia.ATTN_ERR_SHAPE),     # H * d > 2^24
 ])
 def test_attn_fwd_fp8_rejects(kw, status):
     assert fp8(**kw) == status

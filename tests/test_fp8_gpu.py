@@ -47,7 +47,7 @@ def test_worked_example_fp8():
     assert np.abs(L - math.log(3.0)).max() < 2e-6
 
 
-@pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 255, 257, 300])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 255, 257, 300, 511, 513])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_small_shapes_fp8(N, causal):
     q, k, v, qs, ks, vs = _quantized(N + 31 * causal, (2, N, 3, 128))
