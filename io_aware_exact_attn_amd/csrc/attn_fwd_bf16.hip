@@ -254,11 +254,15 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   const bool lacc_swapped = lane >= 16 && lane < 48;
   const float inv_c = 1.f / c;
 
-  // ---- prologue: K(0), K(1), V(0) resident, S(0) computed from 0 (every wave)
+  // ---- prologue: K(0), K(1) (first group) and V(0) (second group)
+  // resident, S(0) computed from 0 (every wave)
   if (n_iter > 0) {
-    issue_tile(kg, 0, 0);
-    issue_tile(vg, 2, 0);
-    if (n_iter > 1) issue_tile(kg, 1, 1);
+    if (!lag) {
+      issue_tile(kg, 0, 0);
+      if (n_iter > 1) issue_tile(kg, 1, 1);
+    } else {
+      issue_tile(vg, 2, 0);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -438,24 +442,45 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   const float lx_tot = __uint_as_float(swx[0]) + __uint_as_float(swx[1]);
   const int64_t lse_base = PACKED ? ((int64_t)h * a.N + seq_start) : ((int64_t)(b * a.H + h) * a.N);
   const int t = wq0 + l32;
-  if (t < seq_len) {
-    const bool any = l_tot > 0.f;
-    const float inv = any ? 1.f / l_tot : 0.f;
-    if (hl == 0) a.lse[lse_base + t] = any ? kLn2 * (m_run * c + __log2f(lx_tot)) : -INFINITY;
-    const int64_t orow = (int64_t)(seq_start + t) * rs + head_off;
+  const bool any = l_tot > 0.f;
+  const float inv = any ? 1.f / l_tot : 0.f;
+  if (t < seq_len && hl == 0) a.lse[lse_base + t] = any ? kLn2 * (m_run * c + __log2f(lx_tot)) : -INFINITY;
+  if constexpr (OUT_F32) {
+    if (t < seq_len) {
+      const int64_t orow = (int64_t)(seq_start + t) * rs + head_off;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + g * 8 + hl * 4;
+          *(f32x4*)((float*)a.o + orow + d) = (f32x4){oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv,
+                                                      oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv};
+        }
+    }
+  } else {
+    // bf16 O goes out through LDS (free after the last barrier): each wave
+    // writes its 32 rows into its own slice (16-byte granules XOR-swizzled by
+    // row), then reads them back in row order, so every global store covers
+    // whole 16-byte pieces of consecutive rows.
+    constexpr int NG = ROWB / 16;              // 16-byte granules per row
+    char* slice = smem + wave * 32 * ROWB;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + g * 8 + hl * 4;
-        const float o0 = oacc[db][g * 4 + 0] * inv, o1 = oacc[db][g * 4 + 1] * inv;
-        const float o2 = oacc[db][g * 4 + 2] * inv, o3 = oacc[db][g * 4 + 3] * inv;
-        if constexpr (OUT_F32) {
-          *(f32x4*)((float*)a.o + orow + d) = (f32x4){o0, o1, o2, o3};
-        } else {
-          *(u32x2*)((uint16_t*)a.o + orow + d) = (u32x2){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-        }
+        const int G = db * 4 + g;
+        *(u32x2*)(slice + l32 * ROWB + ((G ^ (l32 & (NG - 1))) << 4) + hl * 8) =
+            (u32x2){pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv),
+                    pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv)};
       }
+#pragma unroll
+    for (int k = 0; k < 32 * NG / 64; ++k) {
+      const int cidx = k * 64 + lane;
+      const int row = cidx / NG, G = cidx % NG;
+      const u32x4 x = *(const u32x4*)(slice + row * ROWB + ((G ^ (row & (NG - 1))) << 4));
+      if (wq0 + row < seq_len)
+        *(u32x4*)((uint16_t*)a.o + (int64_t)(seq_start + wq0 + row) * rs + head_off + G * 8) = x;
+    }
   }
 }
 
