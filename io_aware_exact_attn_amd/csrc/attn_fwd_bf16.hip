@@ -459,17 +459,20 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     }
   } else {
     // bf16 O goes out through LDS (free after the last barrier): each wave
-    // writes its 32 rows into its own slice (16-byte granules XOR-swizzled by
-    // row), then reads them back in row order, so every global store covers
-    // whole 16-byte pieces of consecutive rows.
+    // writes its 32 rows into its own slice, then reads them back in row
+    // order, so every global store covers whole 16-byte pieces of
+    // consecutive rows.  A row's 16-byte granules are XOR-swizzled by the row
+    // and its two 8-byte halves swapped on odd multiples of NG rows, so the
+    // 8-byte writes of the 32 rows spread over all banks.
     constexpr int NG = ROWB / 16;              // 16-byte granules per row
     char* slice = smem + wave * 32 * ROWB;
+    const int wflip = (l32 / NG) & 1;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int G = db * 4 + g;
-        *(u32x2*)(slice + l32 * ROWB + ((G ^ (l32 & (NG - 1))) << 4) + hl * 8) =
+        *(u32x2*)(slice + l32 * ROWB + ((G ^ (l32 & (NG - 1))) << 4) + ((hl ^ wflip) << 3)) =
             (u32x2){pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv),
                     pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv)};
       }
@@ -478,8 +481,10 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       const int cidx = k * 64 + lane;
       const int row = cidx / NG, G = cidx % NG;
       const u32x4 x = *(const u32x4*)(slice + row * ROWB + ((G ^ (row & (NG - 1))) << 4));
+      const bool flip = (row / NG) & 1;
+      const u32x4 y = flip ? (u32x4){x[2], x[3], x[0], x[1]} : x;
       if (wq0 + row < seq_len)
-        *(u32x4*)((uint16_t*)a.o + (int64_t)(seq_start + wq0 + row) * rs + head_off + G * 8) = x;
+        *(u32x4*)((uint16_t*)a.o + (int64_t)(seq_start + wq0 + row) * rs + head_off + G * 8) = y;
     }
   }
 }
