@@ -91,12 +91,41 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, int bid, int& h, i
     seq_len = a.N;
     return true;
   } else {
+    const int lane = threadIdx.x & 63;
+    if (a.B <= 64) {
+      // Up to 64 documents, one per lane: documents go out longest first,
+      // each with its q blocks longest first, and the head as the minor
+      // index (so a document's blocks run together on an XCD for locality).
+      // The last workgroups to start are those of the shortest documents.
+      const int t = bid / a.H;
+      h = bid - t * a.H;
+      const int len = lane < a.B ? a.cu_seqlens[lane + 1] - a.cu_seqlens[lane] : 0;
+      const int nb = len > 0 ? (len + BM - 1) / BM : 0;
+      int rank = 0;                            // documents before this one in the order
+      for (int f = 0; f < a.B; ++f) {
+        const int lf = __builtin_amdgcn_readlane(len, f);
+        rank += (lf > len) || (lf == len && f < lane);
+      }
+      int first = 0;                           // items before this document's first
+      for (int f = 0; f < a.B; ++f)
+        first += (__builtin_amdgcn_readlane(rank, f) < rank) ? __builtin_amdgcn_readlane(nb, f) : 0;
+      const unsigned long long m = __ballot(lane < a.B && t >= first && t < first + nb);
+      if (m == 0) return false;
+      const int doc = __ffsll((long long)m) - 1;
+      const int r = t - __builtin_amdgcn_readlane(first, doc);
+      const int nbd = __builtin_amdgcn_readlane(nb, doc);
+      seq_start = a.cu_seqlens[doc];
+      seq_len = __builtin_amdgcn_readlane(len, doc);
+      qblk = CAUSAL ? (nbd - 1 - r) : r;
+      b = doc;
+      return true;
+    }
+    // more documents: each head's slots in document order, per-XCD contiguous
     const int lb = logical_block(bid, a.per_xcd);
     if (lb >= a.n_work) return false;
     h = lb / a.slots;
     const int s = lb - h * a.slots;
     b = 0;
-    const int lane = threadIdx.x & 63;
     int base = 0;
     for (int e0 = 0; e0 < a.B; e0 += 64) {
       const int e = e0 + lane;
