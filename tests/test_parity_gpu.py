@@ -90,6 +90,21 @@ def test_small_varlen(d, causal, out):
     _check(q, k, v, float(np.float32(1 / math.sqrt(d))), causal, out, cu=cu)
 
 
+@pytest.mark.parametrize("n_docs", [63, 64, 65, 150])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_many_documents(n_docs, causal):
+    """The kernel orders up to 64 documents longest first (one lane ranks
+    each) and keeps a plain per-XCD order beyond that: both sides of the
+    limit, with lengths 1..300 including ties and empty documents."""
+    rng = np.random.default_rng(900 + n_docs + causal)
+    lengths = rng.integers(1, 300, n_docs)
+    lengths[::7] = 64                    # ties
+    lengths[3] = 0                       # an empty document
+    cu = W.cu_seqlens_from_lengths(lengths)
+    q, k, v = _case(910 + n_docs + causal, (int(cu[-1]), 2, 64))
+    _check(q, k, v, 0.125, causal, "f32", cu=cu)
+
+
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 1e-3, 0.9])
 def test_scale_values(scale):
     q, k, v = _case(77, (1, 200, 2, 64))
