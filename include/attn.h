@@ -123,12 +123,14 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  *               fp32 [B][H][ceil(N / 128)]: token t of (b, h) has the value
  *               e4m3(byte) * scale[b][h][t / 128].
  *   o           bf16 [B][N][H][128];  lse fp32 [B][H][N].
- *   The probabilities P enter the P.V contraction as e4m3 as well, in tiles
- *   of 128 query rows with a fixed scale of 2^8 (P <= 1 after the running
- *   maximum is subtracted, so no data-dependent scale is needed; a data-
- *   dependent one would read future keys).  P is carried as two e4m3 terms
- *   (P ~ hi + lo, hi = e4m3(P * 2^8) / 2^8, lo = e4m3((P - hi) * 2^12) / 2^12);
- *   the normaliser l is summed from the unquantised fp32 P.  Scales must be
+ *   The probabilities P enter the P.V contraction as e4m3 as well, with one
+ *   power-of-two scale 2^E per query row and 64-key tile, E the smallest
+ *   integer with the row's weights in that tile summing to less than 2^E
+ *   (weights of masked keys are 0, so a scale never depends on keys the row
+ *   may not see).  P is carried as two e4m3 terms, P ~ hi + lo with
+ *   hi = e4m3(P * 2^(8-E)) * 2^(E-8) and lo = e4m3((P - hi) * 2^(12-E)) *
+ *   2^(E-12), each rounded to nearest: about 8 significant bits, as bf16.
+ *   The normaliser l is summed from the unquantised fp32 P.  Scales must be
  *   positive, finite and normal.
  *   Other arguments as attn_fwd; cu_seqlens must be NULL.  H * d must not
  *   exceed 2^24 (ATTN_ERR_SHAPE).

@@ -11,22 +11,26 @@
 // wave's 32 query rows and a 64-key tile each lie inside one 128-token block,
 // so each contraction sees one scale per operand and the dequantisation
 // factors out of the MFMA: S = scale * sq * sk * (Q^ K^T), and a tile's
-// P.V contribution carries one sv.  The accumulator is kept in units of the
-// current tile's sv; moving to a tile with another sv rescales it together
-// with the running-maximum rescale.  No scale is shared across blocks of 128
+// P.V contribution carries one sv.  No scale is shared across blocks of 128
 // tokens, so a token never influences the scale of an earlier block (the
 // causal-leakage concern of "FLAMIA: Blackwell Üzerinde Hızlı ve Nedensel
 // Olarak Güvenli Eğitim İçin Flash Mikro-Ölçeklemeli Dikkat Mekanizması",
 // section "Uzun Bağlamlarda Dikkat (Attention) Maliyeti ve Blackwell
 // Mimarisi").
 //
-// P for the P.V contraction.  The reference maximum moves with every tile,
-// so 0 <= P <= 1 and a fixed scale suffices (a data-dependent one would read
-// future keys of the same tile).  P is carried as two e4m3 terms per element:
-// hi = e4m3(P * 2^8), lo = e4m3((P - hi / 2^8) * 2^12); the MFMA's E8M0 operand
-// scales apply the 2^-8 and 2^-12, so both terms accumulate into one fp32
-// accumulator.  l sums the unquantised fp32 P.
-//
+// P for the P.V contraction.  The reference maximum m is lazy, as in the
+// bf16 kernel: a tile's weights are formed against the current m, which moves
+// only when some lane's weights sum to more than 2^64 (and on a row's first
+// tile).  P enters P.V as two e4m3 terms with a power-of-two scale per query
+// (both lanes that hold its two 32-key halves use it): with the query's 64
+// weights in the tile summing to less than 2^E, hi = e4m3(P 2^(8-E)) and
+// lo = e4m3((P - hi 2^(E-8)) 2^(12-E)), and the MFMA's per-column E8M0 operand
+// scales apply 2^(E-8) and 2^(E-12) back.  The
+// tile's V scale joins them: its power-of-two part in the same E8M0 scale,
+// the rest f = sv / 2^e in [1, 2) in the exponent of the weights (P' = P f).
+// The accumulator therefore stays in real units, with no per-tile rescale,
+// and the scale of a tile's P depends on that tile only.  l sums the
+// unquantised fp32 P.
 // MI355X mapping: v_mfma_scale_f32_32x32x64_f8f6f4 for S^T = K^ Q^T and
 // O^T = V^T P^T (every lane owns one query column, as in the bf16 kernel);
 // direct global->LDS loads of K/V tiles into double-buffered, swizzled LDS;
@@ -46,8 +50,7 @@ constexpr int ROWB = D;         // bytes per K/V row
 constexpr int TILE = BN * ROWB; // 8 KB
 constexpr int CPW = TILE / 1024 / NW;
 constexpr uint32_t kScaleOne = 0x7f7f7f7fu;     // E8M0 2^0 in every byte
-constexpr uint32_t kScaleHi = 0x77777777u;      // E8M0 2^-8
-constexpr uint32_t kScaleLo = 0x73737373u;      // E8M0 2^-12
+constexpr float kLazyMax = 0x1p64;              // as in the bf16 kernel
 
 // 16-byte-granule swizzle of a 128-byte row (a permutation of row bits 1..3):
 // conflict-free for the K fragment reads (16 consecutive rows, one granule)
@@ -70,23 +73,6 @@ __device__ __forceinline__ f32x16 mfma(const i32x8& a, const i32x8& b, const f32
 }  // namespace fp8
 
 template <int P> struct F8Parity { static constexpr int value = P; };
-
-// P for elements j0, j0 + 1 of the P^T operand (S register j0 / 16, j0 % 16):
-// p = exp2(s * ct - ms); the hi byte is e4m3(p * 2^8), the lo byte e4m3 of the
-// rounding residual times 2^4 (i.e. of (p - hi / 2^8) * 2^12).  HIGH selects
-// the upper 16 bits of the packed words.
-template <bool HIGH>
-__device__ __forceinline__ void quant_pair(const f32x16 (&s)[2], int j0, float ct, float ms,
-                                           int& hw, int& lw, float& lsum) {
-  const float p0 = fast_exp2(__builtin_fmaf(s[j0 >> 4][j0 & 15], ct, -ms));
-  const float p1 = fast_exp2(__builtin_fmaf(s[(j0 + 1) >> 4][(j0 + 1) & 15], ct, -ms));
-  lsum += p0 + p1;
-  const float x0 = p0 * 256.f, x1 = p1 * 256.f;
-  hw = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, hw, HIGH);
-  const float h0 = __builtin_amdgcn_cvt_f32_fp8(hw, HIGH ? 2 : 0);
-  const float h1 = __builtin_amdgcn_cvt_f32_fp8(hw, HIGH ? 3 : 1);
-  lw = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - h0) * 16.f, (x1 - h1) * 16.f, lw, HIGH);
-}
 
 template <bool CAUSAL>
 __global__ void __launch_bounds__(fp8::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -135,28 +121,30 @@ attn_fwd_fp8_kernel(FwdArgs a) {
     }
   }
 
-  // ---- direct global -> LDS tile loads (as in the bf16 kernel)
+  // ---- K/V tiles: HBM -> LDS (buffer_load_dwordx4 ... lds, as in the bf16
+  // kernel); the buffer size ends at the end of the sequence, so rows past it
+  // read as zeros
   uint32_t lane_off[CPW];
-  int lane_row[CPW];
 #pragma unroll
   for (int cc = 0; cc < CPW; ++cc) {
     const int byte = (wave * CPW + cc) * 1024 + lane * 16;
     const int row = byte / ROWB;
     const int g = ((byte % ROWB) >> 4) ^ swz(row);
-    lane_row[cc] = row;
     lane_off[cc] = (uint32_t)((int64_t)row * rs + head_off + g * 16);
   }
-  auto issue_tile = [&](const uint8_t* __restrict__ src, int buf, int j) {
+  [[maybe_unused]] const uint32_t row_bytes = (uint32_t)rs;
+  auto issue_tile = [&](const uint8_t* __restrict__ src, int buf, int j) __attribute__((always_inline)) {
+#if __HIP_DEVICE_COMPILE__   // the 16-byte LDS DMA form exists only for the device target
     const int kv0 = j * BN;
-    const char* base = (const char*)(src + (int64_t)(seq_start + kv0) * rs);
-    char* dst = smem + buf * TILE + wave * CPW * 1024;
+    const uint32_t nrec = (uint32_t)min(seq_len - kv0, BN) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)src + (uint64_t)(uint32_t)(seq_start + kv0) * row_bytes), (short)0, (int)nrec,
+        kBufferFlags);
 #pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int over = max(0, kv0 + lane_row[cc] - (seq_len - 1));
-      const uint32_t off = lane_off[cc] - (uint32_t)((int64_t)over * rs);
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(base + off),
-                                       (IAEA_LDS void*)(dst + cc * 1024), 16, 0, 0);
-    }
+    for (int cc = 0; cc < CPW; ++cc)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (IAEA_LDS void*)(smem + buf * TILE + (wave * CPW + cc) * 1024),
+                                               16, lane_off[cc], 0, 0, 0);
+#endif
   };
 
   // ---- loop-invariant LDS read offsets.  K fragment: row kb*32 + l32, bytes
@@ -188,9 +176,8 @@ attn_fwd_fp8_kernel(FwdArgs a) {
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = (f32x16){};
-  float m_run = -INFINITY;   // reference maximum, in the exp2 domain (scales folded in)
-  float l_run = 0.f;
-  float sv_ref = 1.f;        // the accumulator holds O * l / sv_ref
+  float m_run = -INFINITY;   // lazy reference maximum, in the exp2 domain (scales folded in)
+  float l_run = 0.f;         // this lane's sum of the fp32 weights P (half of the row's keys)
 
   auto step = [&](auto par, int it) {
     constexpr int P = decltype(par)::value;
@@ -205,62 +192,106 @@ attn_fwd_fp8_kernel(FwdArgs a) {
       const float sk = ks[kv0 / 128];
       const float sv = vs[kv0 / 128];
       const float ct = cq * sk;
+      // sv = f 2^esv with f in [1, 2)
+      const float f = 2.f * __builtin_amdgcn_frexp_mantf(sv);
+      const int esv = __builtin_amdgcn_frexp_expf(sv) - 1;
+      const float lf = __log2f(f);
 
-      // S^T for the two 32-key halves of the tile
+      // S^T for the two 32-key halves of the tile, masked
       f32x16 s[2];
+      auto scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int dc = 0; dc < 2; ++dc) {
-          const u32x4 x0 = *(const u32x4*)(kt + kb * 32 * ROWB + koff[dc][0]);
-          const u32x4 x1 = *(const u32x4*)(kt + kb * 32 * ROWB + koff[dc][1]);
-          const i32x8 kf = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                            (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-          s[kb] = mfma(kf, qf[dc], dc == 0 ? (f32x16){} : s[kb], kScaleOne);
+          for (int dc = 0; dc < 2; ++dc) {
+            const u32x4 x0 = *(const u32x4*)(kt + kb * 32 * ROWB + koff[dc][0]);
+            const u32x4 x1 = *(const u32x4*)(kt + kb * 32 * ROWB + koff[dc][1]);
+            const i32x8 kf = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                              (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+            s[kb] = mfma(kf, qf[dc], dc == 0 ? (f32x16){} : s[kb], kScaleOne);
+          }
         }
-      }
-      const bool edge = (kv0 + BN > seq_len) || (CAUSAL && kv0 + BN - 1 > wq0);
-      if (edge) {
-        const int lim = (CAUSAL ? min(wq0 + l32, seq_len - 1) : seq_len - 1) - (kv0 + hl * 4);
+        if ((kv0 + BN > seq_len) || (CAUSAL && kv0 + BN - 1 > wq0)) {
+          const int lim = (CAUSAL ? min(wq0 + l32, seq_len - 1) : seq_len - 1) - (kv0 + hl * 4);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) s[kb][r] = -INFINITY;
+        }
+      };
+      // P' = exp2(s ct - m + log2 f) = P f in place of the scores; returns the
+      // lane's sum of P'
+      auto weights = [&]() __attribute__((always_inline)) -> float {
+        const float shift = m_run - lf;
+        float x0 = 0.f, x1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) s[kb][r] = -INFINITY;
-      }
-
-      // running maximum (moved every tile), rescale by exp(m - m_new) and sv_ref / sv
-      float mx = fmaxf(s[0][0], s[1][0]);
+          for (int r = 0; r < 16; r += 2) {
+            s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], ct, -shift));
+            s[kb][r + 1] = fast_exp2(__builtin_fmaf(s[kb][r + 1], ct, -shift));
+            if (r & 2) x1 += s[kb][r] + s[kb][r + 1];
+            else       x0 += s[kb][r] + s[kb][r + 1];
+          }
+        return x0 + x1;
+      };
+      scores();
+      float lx = weights();
+      const bool first = m_run == -INFINITY;
+      if (__ballot(lx > kLazyMax || first) != 0) {
+        // rare: the reference moves to the tile maximum (the scores are formed
+        // again, their registers now hold weights)
+        scores();
+        float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-      {
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      const float m_new = fmaxf(m_run, mx == -INFINITY ? -INFINITY : mx * ct);
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-      const float acc_mul = alpha * (sv_ref / sv);
-      m_run = m_new;
-      sv_ref = sv;
-      l_run *= alpha;
+        const float mxs = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * ct;
+        const float m_new = first ? mxs : m_run + fmaxf(mxs - m_run, 0.f);
+        const float alpha = first ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= acc_mul;
-      const float ms = (m_new == -INFINITY) ? 0.f : m_new;
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+        lx = weights();
+      }
+      l_run = __builtin_fmaf(lx, 1.f / f, l_run);
 
-      // P = exp2(s * ct - m) in [0, 1]; two e4m3 terms with fixed scales
+      // P' as two e4m3 terms with the query's power-of-two scale 2^E above the
+      // sum of its 64 weights in this tile: hi = e4m3(P' 2^(8-E)),
+      // lo = e4m3((P' - hi 2^(E-8)) 2^(12-E)).  The conversions apply the
+      // power-of-two part of their scale operand.  The matrix instruction takes
+      // one B scale per column, so both lanes holding a query's 32-key halves
+      // (l and l ^ 32) must quantise against the same E.
+      const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lx), __float_as_uint(lx), false, false);
+      const float lq = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+      const int E = lq > 0.f ? __builtin_amdgcn_frexp_expf(lq) : 0;
+      const float sh = __builtin_amdgcn_ldexpf(1.f, E - 8), sl = __builtin_amdgcn_ldexpf(1.f, E - 12);
       i32x8 phi, plo;
-      float lsum = 0.f;
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        int hw = 0, lw = 0;
-        quant_pair<false>(s, 4 * w, ct, ms, hw, lw, lsum);
-        quant_pair<true>(s, 4 * w + 2, ct, ms, hw, lw, lsum);
-        phi[w] = hw;
-        plo[w] = lw;
+        // p index j -> S register j / 16, j % 16: bytes 0..3 of word w are p[4w .. 4w + 3]
+        const int j = 4 * w, kb = j >> 4, r = j & 15;
+        s16x2 h2 = {0, 0}, l2 = {0, 0};
+        h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, s[kb][r], s[kb][r + 1], sh, false);
+        h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, s[kb][r + 2], s[kb][r + 3], sh, true);
+        const uint32_t hw = __builtin_bit_cast(uint32_t, h2);
+        const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, sh, false);
+        const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, sh, true);
+        l2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l2, s[kb][r] - b01[0], s[kb][r + 1] - b01[1], sl, false);
+        l2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l2, s[kb][r + 2] - b23[0], s[kb][r + 3] - b23[1], sl, true);
+        phi[w] = (int)hw;
+        plo[w] = (int)__builtin_bit_cast(uint32_t, l2);
       }
-      l_run += lsum;
+      // E8M0 scales of the P^T operand: 2^(E-8) and 2^(E-12) times the
+      // power-of-two part 2^esv of the V scale (clamped to the format's range;
+      // a clamp only touches tiles whose weights are ~2^-100 of the row's)
+      // (the byte is repeated in all four operand bytes, as the fixed scales are)
+      const uint32_t ehi = (uint32_t)min(max(127 + E - 8 + esv, 0), 254) * 0x01010101u;
+      const uint32_t elo = (uint32_t)min(max(127 + E - 12 + esv, 0), 254) * 0x01010101u;
 
-      // O^T += V^T P^T (hi and lo terms), 64 keys per MFMA
+      // O^T += V^T P'^T (hi and lo terms), 64 keys per MFMA
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         i32x8 vf;
@@ -270,11 +301,10 @@ attn_fwd_fp8_kernel(FwdArgs a) {
           vf[2 * t] = x[0];
           vf[2 * t + 1] = x[1];
         }
-        oacc[db] = mfma(vf, phi, oacc[db], kScaleHi);
-        oacc[db] = mfma(vf, plo, oacc[db], kScaleLo);
+        oacc[db] = mfma(vf, phi, oacc[db], ehi);
+        oacc[db] = mfma(vf, plo, oacc[db], elo);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
@@ -282,20 +312,19 @@ attn_fwd_fp8_kernel(FwdArgs a) {
     issue_tile(kg, 0, 0);
     issue_tile(vg, 2, 0);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int it = 0; it < n_iter; it += 2) {
     step(F8Parity<0>{}, it);
     if (it + 1 < n_iter) step(F8Parity<1>{}, it + 1);
   }
 
-  // ---- epilogue: O = u / l (u in units of sv_ref), LSE = ln2 * (m + log2 l)
+  // ---- epilogue: O = u / l, LSE = ln2 * (m + log2 l)
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   const int t = wq0 + l32;
   if (t < seq_len) {
     const bool any = l_tot > 0.f;
-    const float mul = any ? sv_ref / l_tot : 0.f;
+    const float mul = any ? 1.f / l_tot : 0.f;
     if (hl == 0)
       a.lse[(int64_t)(b * a.H + h) * a.N + t] = any ? kLn2 * (m_run + __log2f(l_tot)) : -INFINITY;
     const int64_t orow = (int64_t)(seq_start + t) * rs + head_off;   // element index (D per token-head)
