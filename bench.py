@@ -97,6 +97,68 @@ def counters_from_profiles(wname):
     return t
 
 
+def power_pass(step, ms):
+    """Board power and shader clock while the kernel runs back to back.
+
+    Runs about 0.6 s of launches (untimed, after the timed passes) while a
+    thread reads the board's hwmon power1_input (microwatts) and the current
+    level of pp_dpm_sclk every 10 ms; samples from the first fifth of the
+    pass (the ramp) are dropped.  Returns None where sysfs has no reading."""
+    import glob
+    import threading
+
+    import torch
+    pin = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+    if not pin:
+        return None
+    cap_path = pin[0].replace("power1_input", "power1_cap")
+    sclk_path = os.path.join(os.path.dirname(os.path.dirname(os.path.dirname(pin[0]))), "pp_dpm_sclk")
+
+    def read_sclk():
+        try:
+            for line in open(sclk_path):
+                if "*" in line:
+                    return float(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            pass
+        return None
+
+    n = max(20, int(600.0 / max(ms, 1e-3)))
+    watts, mhz = [], []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                watts.append(int(open(pin[0]).read()) / 1e6)
+            except (OSError, ValueError):
+                pass
+            f = read_sclk()
+            if f is not None:
+                mhz.append(f)
+            time.sleep(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    watts = watts[len(watts) // 5:]
+    mhz = mhz[len(mhz) // 5:]
+    if not watts:
+        return None
+    try:
+        cap = int(open(cap_path).read()) / 1e6
+    except (OSError, ValueError):
+        cap = None
+    return {"board_w_median": round(float(np.median(watts)), 1), "board_w_max": round(max(watts), 1),
+            "cap_w": cap, "sclk_mhz_median": round(float(np.median(mhz)), 0) if mhz else None,
+            "samples": len(watts), "launches": n,
+            "source": "hwmon power1_input and pp_dpm_sclk, sampled every 10 ms during untimed back-to-back launches"}
+
+
 def cpu_baseline(w, inp, O_gpu, budget_s):
     """The fp64 oracle, as it stands, on whole heads of the workload until about
     ``budget_s`` seconds of CPU time are spent; scaled to TFLOP/s."""
@@ -143,6 +205,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-power", dest="power", action="store_false",
+                    help="skip the untimed power/clock sampling pass")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="size of the scratch write that evicts the caches before each launch "
                          "of the cache-cold timing pass (0 skips that pass)")
@@ -259,6 +323,8 @@ def main():
             cold.append(a_.elapsed_time(b_))
         del scratch
 
+    power = power_pass(step, ms) if args.power else None
+
     F = flops(w, inp.get("lengths"))
     F_pairs = exact_pair_flops(w, inp.get("lengths"))
     F_tiles = tile_flops(w, inp.get("lengths"))
@@ -299,6 +365,7 @@ def main():
                    "cache_cold_flush_mib": args.flush_mib,
                    "cache_cold_ms_median": round(float(np.median(cold)), 5) if cold else None,
                    "cache_cold_tflops": round(F / (float(np.median(cold)) * 1e-3) / 1e12, 2) if cold else None},
+        "power": power,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
