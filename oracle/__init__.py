@@ -19,10 +19,20 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
                                bit patterns
   dequantize_e4m3_blocks       pinned: exact round trip with scale 1 blocks and
                                hand-built blocks
+  quantize.e4m3_encode         pinned (tests/test_quantize_oracle.py): every
+                               finite byte round-trips, hand-computed midpoints
+                               and saturation, torch's float8_e4m3fn cast
+  quantize.quantize_blocks     pinned: hand-built blocks, block maximum -> 448,
+                               all-zero blocks, packed = per-document, distinct
+                               scale slots, dequantisation error bound; planted
+                               mistakes each trip a pin
+  quantize.dequantize_blocks   pinned: the dequantisation error bound above
 """
 from .exact import (attention, attention_rows, online_softmax_states,
                         e4m3_decode, bf16_decode, dequantize_e4m3_blocks,
                         visible_keys)
+from . import quantize
 
 __all__ = ["attention", "attention_rows", "online_softmax_states",
-           "e4m3_decode", "bf16_decode", "dequantize_e4m3_blocks", "visible_keys"]
+           "e4m3_decode", "bf16_decode", "dequantize_e4m3_blocks", "visible_keys",
+           "quantize"]
