@@ -45,7 +45,8 @@
  *   < 2^31 * d); scale finite (any sign, zero allowed).
  *   attn_fwd:     bf16 q/k/v; o bf16 (ATTN_BF16) or fp32 (ATTN_BF16_OUT_F32).
  *   attn_fwd_fp8: e4m3 q/k/v with per-128-token block scales, o bf16, d = 128,
- *                 fixed length only (cu_seqlens must be NULL).
+ *                 fixed length or packed documents.
+ *   attn_quantize_fp8: bf16 -> e4m3 with those block scales, d in {64, 128}.
  *   Anything else returns an error; there is no fallback path.
  *
  * Ownership and concurrency
@@ -80,7 +81,7 @@ typedef enum {
     ATTN_ERR_NULL = 1,         /* a required pointer is NULL                         */
     ATTN_ERR_SHAPE = 2,        /* B, H or N < 1, or the tensors are too large        */
                                /* (B*N*H >= 2^31; bf16: H*d > 2^24)                  */
-    ATTN_ERR_UNSUPPORTED = 3,  /* d, dtype, causal flag or packed fp8 not supported  */
+    ATTN_ERR_UNSUPPORTED = 3,  /* d, dtype or causal flag not supported              */
     ATTN_ERR_SCALE = 4,        /* scale is NaN or infinite                           */
     ATTN_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned                   */
     ATTN_ERR_HIP = 6           /* the kernel launch failed                           */
@@ -110,19 +111,26 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                       const int32_t* cu_seqlens, int dtype, void* stream);
 
 /*
- * attn_fwd_fp8 - block-scaled fp8 exact attention forward (d = 128, fixed
- * length).  The FP8 path with per-tile scales follows the FlashAttention-3
+ * attn_fwd_fp8 - block-scaled fp8 exact attention forward (d = 128).  The FP8
+ * path with per-tile scales follows the FlashAttention-3
  * part of "FlashAttention, pelatihan multi-GPU, dan kuantisasi bobot",
  * section 1 (block quantisation: each tile carries its own scale); the scale
  * blocks never mix tokens of different 128-token blocks, the causal-leakage
  * concern of the FLAMIA page (sections "Uzun Bağlamlarda Dikkat (Attention)
  * Maliyeti ve Blackwell Mimarisi" and "FLAMIA Mimarisi ve Temel Tasarım
  * İlkeleri").
- *   q, k, v     OCP e4m3 ("e4m3fn") bytes, [B][N][H][128].
+ *   q, k, v     OCP e4m3 ("e4m3fn") bytes, [B][N][H][128] (packed [N][H][128]).
  *   q_scale, k_scale, v_scale
- *               fp32 [B][H][ceil(N / 128)]: token t of (b, h) has the value
- *               e4m3(byte) * scale[b][h][t / 128].
- *   o           bf16 [B][N][H][128];  lse fp32 [B][H][N].
+ *               fixed length: fp32 [B][H][ceil(N / 128)]; token t of (b, h)
+ *               has the value e4m3(byte) * scale[b][h][t / 128].
+ *               packed: fp32 [H][ceil(N / 128) + B]; the 128-token blocks
+ *               restart at every document's first token, and token
+ *               cu_seqlens[b] + t of document b (0 <= t < its length) has the
+ *               value e4m3(byte) * scale[h][cu_seqlens[b] / 128 + b + t / 128].
+ *               Distinct blocks have distinct slots; other slots are not read.
+ *               attn_quantize_fp8 writes both layouts.
+ *   o           bf16 [B][N][H][128] (packed [N][H][128]);  lse fp32 [B][H][N]
+ *               (packed [H][N]).
  *   The probabilities P enter the P.V contraction as e4m3 as well, with one
  *   power-of-two scale 2^E per query row and 64-key tile, E the smallest
  *   integer with the row's weights in that tile summing to less than 2^E
@@ -132,13 +140,38 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  *   2^(E-12), each rounded to nearest: about 8 significant bits, as bf16.
  *   The normaliser l is summed from the unquantised fp32 P.  Scales must be
  *   positive, finite and normal.
- *   Other arguments as attn_fwd; cu_seqlens must be NULL.  H * d must not
- *   exceed 2^24 (ATTN_ERR_SHAPE).
+ *   Other arguments as attn_fwd.  H * d must not exceed 2^24 (ATTN_ERR_SHAPE).
  */
 ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
                           const float* q_scale, const float* k_scale, const float* v_scale,
                           void* o, float* lse, int B, int H, int N, int d, float scale,
                           int causal, const int32_t* cu_seqlens, void* stream);
+
+/*
+ * attn_quantize_fp8 - block-scaled e4m3 quantisation of a bf16 tensor, the
+ * step upstream of attn_fwd_fp8: the per-tile scales of the FlashAttention-3
+ * part of "FlashAttention, pelatihan multi-GPU, dan kuantisasi bobot"
+ * (section 1), with no scale spanning two 128-token blocks or two documents
+ * (the FLAMIA page, sections "Uzun Bağlamlarda Dikkat (Attention) Maliyeti ve
+ * Blackwell Mimarisi" and "FLAMIA Mimarisi ve Temel Tasarım İlkeleri").  For
+ * every block (up to 128 consecutive tokens of one sequence or document and
+ * one head, all d):
+ *     s = amax / 448 in fp32 (s = 1 when the block is all zero),
+ *     y = e4m3(x / s): x / s rounded to fp32, then to the nearest e4m3 value
+ *         (ties to the even mantissa; 448 is the largest).
+ *   x           bf16 [B][N][H][d] (packed [N][H][d]), finite.
+ *   y           e4m3 bytes, same layout; fully overwritten.
+ *   scales      fp32 [B][H][ceil(N / 128)] (packed [H][ceil(N / 128) + B]),
+ *               the layouts attn_fwd_fp8 reads; packed slots that no block
+ *               maps to are left untouched.
+ *   B, H, N, d  sizes as attn_fwd; d in {64, 128}.
+ *   cu_seqlens  NULL, or device int32[B + 1] (packed documents).
+ *   stream      HIP stream to enqueue on.
+ *   Errors as attn_fwd (ATTN_ERR_NULL, _SHAPE, _UNSUPPORTED for d, _ALIGN
+ *   for pointers not 16-byte aligned, _HIP).
+ */
+ATTN_API int attn_quantize_fp8(const void* x, void* y, float* scales, int B, int H, int N, int d,
+                               const int32_t* cu_seqlens, void* stream);
 
 /* attn_status_str - static, NUL-terminated description of a status code
  * (unknown codes give "unknown status").  Never NULL; do not free. */

@@ -18,7 +18,7 @@ import os
 __all__ = [
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_SCALE",
     "ATTN_ERR_ALIGN", "ATTN_ERR_HIP", "ATTN_BF16", "ATTN_BF16_OUT_F32", "ATTN_FP8_E4M3",
-    "AttnError", "attn_fwd", "attn_fwd_fp8", "attn_status_str", "attn_kernel_name",
+    "AttnError", "attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_status_str", "attn_kernel_name",
     "library_path", "lib",
 ]
 
@@ -31,7 +31,7 @@ library_path = os.path.join(_HERE, "libattn.so")
 
 if not os.path.exists(library_path):
     raise ImportError(
-        f"{library_path} is missing: build it with `python -m io_aware_exact_attn_amd.build` "
+        f"{library_path} is missing: build it with `python io_aware_exact_attn_amd/build.py` "
         "(there is no non-HIP implementation)")
 
 # PyTorch owns the device memory and the streams handed to the library, and it
@@ -49,6 +49,8 @@ lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _
 lib.attn_fwd.restype = _i
 lib.attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]
 lib.attn_fwd_fp8.restype = _i
+lib.attn_quantize_fp8.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
+lib.attn_quantize_fp8.restype = _i
 lib.attn_status_str.argtypes = [_i]
 lib.attn_status_str.restype = ctypes.c_char_p
 lib.attn_kernel_name.argtypes = [_i, _i, _i, _i, _i]
@@ -113,4 +115,13 @@ def attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale, 
                           int(causal), _ptr(cu_seqlens), _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_fwd_fp8")
+    return st
+
+
+def attn_quantize_fp8(x, y, scales, B, H, N, d, cu_seqlens=None, stream=None, check: bool = True) -> int:
+    """Enqueue the bf16 -> e4m3 block quantisation (see ``attn_quantize_fp8``)."""
+    st = lib.attn_quantize_fp8(_ptr(x), _ptr(y), _ptr(scales), int(B), int(H), int(N), int(d),
+                               _ptr(cu_seqlens), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_quantize_fp8")
     return st

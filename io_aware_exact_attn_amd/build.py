@@ -1,6 +1,8 @@
 """Build the gfx950 attention library ``libattn.so`` in-tree with hipcc.
 
-    python -m io_aware_exact_attn_amd.build          # or build() from Python
+    python io_aware_exact_attn_amd/build.py          # or build() from Python
+
+(run as a file: importing the package loads the library it builds)
 
 Each HIP/C++ source is compiled for gfx950 only, with packed fp32 vector
 instructions disabled, then linked into one shared library next to this file.
@@ -19,7 +21,7 @@ OUT = os.path.join(HERE, "libattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "quantize_fp8.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

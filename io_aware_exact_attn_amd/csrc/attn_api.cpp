@@ -77,14 +77,36 @@ ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
   if (st != ATTN_OK) return st;
   if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_NULL;
   if (d != 128) return ATTN_ERR_UNSUPPORTED;
-  if (cu_seqlens) return ATTN_ERR_UNSUPPORTED;
   // a 64-row K/V tile of all heads (64 * H * d bytes) is addressed with 32-bit offsets
   if ((int64_t)H * d > ((int64_t)1 << 24)) return ATTN_ERR_SHAPE;
   if (!aligned16(q_scale) || !aligned16(k_scale) || !aligned16(v_scale)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
+  // packed: ceil(N / 128) + B workgroup slots and scale slots per head
+  if (cu_seqlens && (int64_t)H * ((N + 127) / 128 + B) + 8 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
   a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
-  a.nsb = (N + 127) / 128;
+  a.cu_seqlens = cu_seqlens;
+  a.nsb = (N + 127) / 128 + (cu_seqlens ? B : 0);
   a.qsign = std::signbit(scale) ? 0x80808080u : 0u;   // e4m3 sign bits
-  const hipError_t e = iaea::launch_attn_fwd_fp8(a, causal == 1, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = iaea::launch_attn_fwd_fp8(a, causal == 1, cu_seqlens != nullptr,
+                                                 reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+ATTN_API int attn_quantize_fp8(const void* x, void* y, float* scales, int B, int H, int N, int d,
+                               const int32_t* cu_seqlens, void* stream) {
+  if (!x || !y || !scales) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * N * H >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(scales)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
+  if (iaea::quantize_fp8_grid(B, H, N, cu_seqlens != nullptr) >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  iaea::QuantArgs a{};
+  a.x = x; a.y = y; a.scales = scales; a.cu_seqlens = cu_seqlens;
+  a.B = B; a.H = H; a.N = N;
+  a.nsb = (N + 127) / 128 + (cu_seqlens ? B : 0);
+  const hipError_t e = iaea::launch_quantize_fp8(a, d, cu_seqlens != nullptr,
+                                                 reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -104,8 +126,10 @@ ATTN_API const char* attn_status_str(int status) {
 ATTN_API const char* attn_kernel_name(int d, int causal, int packed, int dtype, int fp8) {
   if (causal != 0 && causal != 1) return "";
   if (fp8) {
-    if (d != 128 || packed) return "";
-    return causal ? "attn_fwd_fp8_kernel<causal>" : "attn_fwd_fp8_kernel<full>";
+    if (d != 128) return "";
+    static const char* f8[2][2] = {{"attn_fwd_fp8_kernel<full,fixed>", "attn_fwd_fp8_kernel<full,packed>"},
+                                   {"attn_fwd_fp8_kernel<causal,fixed>", "attn_fwd_fp8_kernel<causal,packed>"}};
+    return f8[causal][packed ? 1 : 0];
   }
   if ((d != 64 && d != 128) || (dtype != ATTN_BF16 && dtype != ATTN_BF16_OUT_F32)) return "";
   static const char* names[2][2][2][2] = {

@@ -50,6 +50,16 @@ struct FwdArgs {
   float lse_mul;             // ln 2: LSE = ln2 * (m_scaled + log2 l)
 };
 
+// Arguments of the e4m3 block quantiser.
+struct QuantArgs {
+  const void* x;             // bf16 input, [B][N][H][d] or packed [N][H][d]
+  void* y;                   // e4m3 output, same layout
+  float* scales;             // [B][H][nsb] or packed [H][nsb]
+  const int32_t* cu_seqlens; // packed documents, device, B + 1 entries
+  int B, H, N;
+  int nsb;                   // scale slots per (sequence, head): ceil(N / 128), packed + B
+};
+
 // Undo the round-robin XCD dispatch: consecutive logical indices land on one
 // XCD, so workgroups that run together on an XCD share its L2 (packed
 // documents: a head's documents stay together).

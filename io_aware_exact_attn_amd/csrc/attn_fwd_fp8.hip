@@ -7,7 +7,10 @@
 // pelatihan multi-GPU, dan kuantisasi bobot", section 1) - with the FP8
 // operands and per-tile scales of that section's FlashAttention-3 part.
 //
-// Scales.  Token t of (b, h) holds e4m3(byte) * scale[b][h][t / 128].  A
+// Scales.  Token t of (b, h) holds e4m3(byte) * scale[b][h][t / 128]; for
+// packed documents the blocks restart at each document's first token and
+// token t of document b uses slot cu[b] / 128 + b + t / 128 of the head's row
+// scale[h][.] (t counted from the document start).  A
 // wave's 32 query rows and a 64-key tile each lie inside one 128-token block,
 // so each contraction sees one scale per operand and the dequantisation
 // factors out of the MFMA: S = scale * sq * sk * (Q^ K^T), and a tile's
@@ -74,14 +77,14 @@ __device__ __forceinline__ f32x16 mfma(const i32x8& a, const i32x8& b, const f32
 
 template <int P> struct F8Parity { static constexpr int value = P; };
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool PACKED>
 __global__ void __launch_bounds__(fp8::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 attn_fwd_fp8_kernel(FwdArgs a) {
   using namespace fp8;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
 
   int h, b, seq_start, seq_len, qblk;
-  if (!decode_work<BM, CAUSAL, false>(a, blockIdx.x, h, b,
+  if (!decode_work<BM, CAUSAL, PACKED>(a, blockIdx.x, h, b,
                                       seq_start, seq_len, qblk))
     return;
 
@@ -101,9 +104,12 @@ attn_fwd_fp8_kernel(FwdArgs a) {
   const uint8_t* __restrict__ qg = (const uint8_t*)a.q;
   const uint8_t* __restrict__ kg = (const uint8_t*)a.k;
   const uint8_t* __restrict__ vg = (const uint8_t*)a.v;
-  const float* __restrict__ ks = a.k_scale + (int64_t)(b * a.H + h) * a.nsb;
-  const float* __restrict__ vs = a.v_scale + (int64_t)(b * a.H + h) * a.nsb;
-  const float sq = (wq0 < seq_len) ? a.q_scale[(int64_t)(b * a.H + h) * a.nsb + wq0 / 128] : 1.f;
+  // this (sequence, head)'s scales; packed documents keep block k of
+  // document b in slot seq_start / 128 + b + k of the head's row
+  const int64_t sbase = PACKED ? (int64_t)h * a.nsb + seq_start / 128 + b : (int64_t)(b * a.H + h) * a.nsb;
+  const float* __restrict__ ks = a.k_scale + sbase;
+  const float* __restrict__ vs = a.v_scale + sbase;
+  const float sq = (wq0 < seq_len) ? a.q_scale[sbase + wq0 / 128] : 1.f;
   const float cq = a.c * sq;
 
   // ---- Q fragments: 32 bytes (d = dc*64 + 32*half + 0..31) of this lane's query
@@ -326,7 +332,8 @@ attn_fwd_fp8_kernel(FwdArgs a) {
     const bool any = l_tot > 0.f;
     const float mul = any ? 1.f / l_tot : 0.f;
     if (hl == 0)
-      a.lse[(int64_t)(b * a.H + h) * a.N + t] = any ? kLn2 * (m_run + __log2f(l_tot)) : -INFINITY;
+      a.lse[(PACKED ? (int64_t)h * a.N + seq_start : (int64_t)(b * a.H + h) * a.N) + t] =
+          any ? kLn2 * (m_run + __log2f(l_tot)) : -INFINITY;
     const int64_t orow = (int64_t)(seq_start + t) * rs + head_off;   // element index (D per token-head)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -340,19 +347,25 @@ attn_fwd_fp8_kernel(FwdArgs a) {
   }
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool PACKED>
 static hipError_t launch_fp8(FwdArgs a, hipStream_t st) {
-  a.slots = (a.N + fp8::BM - 1) / fp8::BM;
-  a.n_work = a.B * a.H * a.slots;
+  if (PACKED) {
+    a.slots = (a.N + fp8::BM - 1) / fp8::BM + a.B;
+    a.n_work = a.H * a.slots;
+  } else {
+    a.slots = (a.N + fp8::BM - 1) / fp8::BM;
+    a.n_work = a.B * a.H * a.slots;
+  }
   const int grid = (a.n_work + kXcds - 1) / kXcds * kXcds;
   a.per_xcd = grid / kXcds;
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<CAUSAL>), dim3(grid),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<CAUSAL, PACKED>), dim3(grid),
                          dim3(fp8::NW * 64), args, 0, st);
 }
 
-hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t st) {
-  return causal ? launch_fp8<true>(a, st) : launch_fp8<false>(a, st);
+hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool causal, bool packed, hipStream_t st) {
+  if (packed) return causal ? launch_fp8<true, true>(a, st) : launch_fp8<false, true>(a, st);
+  return causal ? launch_fp8<true, false>(a, st) : launch_fp8<false, false>(a, st);
 }
 
 }  // namespace iaea

@@ -11,7 +11,12 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, int d, bool causal, bool packe
                                 hipStream_t st);
 int bf16_rows_per_workgroup(int d);
 
-// e4m3 q/k/v with per-128-token scales; d = 128; fixed length; o bf16.
-hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t st);
+// e4m3 q/k/v with per-128-token scales; d = 128; o bf16; fixed length or
+// packed documents (document-local scale blocks).
+hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool causal, bool packed, hipStream_t st);
+
+// bf16 -> e4m3 with per-128-token block scales; d in {64, 128}.
+hipError_t launch_quantize_fp8(const QuantArgs& a, int d, bool packed, hipStream_t st);
+int64_t quantize_fp8_grid(int B, int H, int N, bool packed);
 
 }  // namespace iaea

@@ -1,0 +1,146 @@
+// Block-scaled e4m3 quantisation of bf16 tensors for gfx950 (MI355X).
+//
+// The FP8 path of "FlashAttention, pelatihan multi-GPU, dan kuantisasi bobot"
+// (section 1, its FlashAttention-3 part) feeds the attention kernels operands
+// that carry one scale per tile; FLAMIA ("FLAMIA: Blackwell Üzerinde Hızlı ve
+// Nedensel Olarak Güvenli Eğitim İçin Flash Mikro-Ölçeklemeli Dikkat
+// Mekanizması", sections "Uzun Bağlamlarda Dikkat (Attention) Maliyeti ve
+// Blackwell Mimarisi" and "FLAMIA Mimarisi ve Temel Tasarım İlkeleri") counts
+// the quantisation step in its timings and keeps every scale on one side of
+// the causal boundary, for packed documents too.  This kernel is that step:
+// for every block of 128 consecutive tokens of one (sequence or document,
+// head), over all d,
+//     s = amax / 448 in fp32 (1 for an all-zero block),
+//     byte = e4m3(x / s), the quotient rounded once to fp32 and then to the
+//            nearest e4m3 value (ties to even, 448 the largest),
+// with document-local blocks for packed input (a document's first block
+// starts at its first token; block k of document d keeps its scale in slot
+// cu[d] / 128 + d + k of the head's row of scales).
+//
+// MI355X mapping: the work is a stream through HBM (2 bytes read and 1 written
+// per element), so the kernel is built for bandwidth: one 256-thread
+// workgroup per block, 16-byte loads that cover whole 256-byte token rows, the
+// block maximum taken on the bf16 bit patterns (the magnitude order of
+// non-negative floats is the integer order of their bits; v_pk_max_u16 takes
+// two at a time), one wave reduction plus one LDS exchange for the block
+// maximum, the quotient by correctly rounded division, and
+// v_cvt_pk_fp8_f32 for the rounding to e4m3.
+#include "attn_common.h"
+#include "attn_kernels.h"
+
+namespace iaea {
+
+namespace qz {
+constexpr int BLK = 128;   // tokens per scale block
+constexpr int NT = 256;    // threads per workgroup
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+}  // namespace qz
+
+template <int D, bool PACKED>
+__global__ void __launch_bounds__(qz::NT) quantize_fp8_kernel(QuantArgs a) {
+  constexpr int GPR = D / 8;                  // 16-byte bf16 granules per token row
+  constexpr int NG = qz::BLK * GPR / qz::NT;  // granules per thread
+  static_assert(NG * qz::NT == qz::BLK * GPR, "block must split evenly over the threads");
+
+  // workgroup -> (slot, head, sequence)
+  const int bid = blockIdx.x;
+  const int slot = bid % a.nsb;
+  const int rest = bid / a.nsb;
+  const int h = rest % a.H;
+  const int b = rest / a.H;
+  int seq_start, seq_len, blk;
+  int64_t sidx;
+  if constexpr (!PACKED) {
+    blk = slot;
+    seq_start = b * a.N;
+    seq_len = a.N;
+    sidx = ((int64_t)b * a.H + h) * a.nsb + slot;
+  } else {
+    // the document of this slot: the largest doc with cu[doc] / 128 + doc <=
+    // slot (that function of doc is strictly increasing)
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu_seqlens[mid] / qz::BLK + mid <= slot) lo = mid;
+      else hi = mid - 1;
+    }
+    seq_start = a.cu_seqlens[lo];
+    seq_len = a.cu_seqlens[lo + 1] - seq_start;
+    blk = slot - (seq_start / qz::BLK + lo);
+    if (blk * qz::BLK >= seq_len) return;     // no block maps to this slot
+    sidx = (int64_t)h * a.nsb + slot;
+  }
+  const int t0 = blk * qz::BLK;
+  const int nt = min(qz::BLK, seq_len - t0);   // tokens in this block
+  const int64_t rs = (int64_t)a.H * D;         // elements (and output bytes) between tokens
+  const int64_t base = (int64_t)(seq_start + t0) * rs + (int64_t)h * D;
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x + base;
+  uint8_t* __restrict__ y = (uint8_t*)a.y + base;
+  const int tid = threadIdx.x;
+
+  // ---- load the block (a wave covers 64 / GPR whole token rows per step)
+  u32x4 v[NG];
+  qz::u16x2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int g = i * qz::NT + tid;
+    const int row = g / GPR, col = g % GPR;
+    v[i] = row < nt ? *(const u32x4*)(x + row * rs + col * 8) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(qz::u16x2, v[i][w] & 0x7fff7fffu));
+  }
+
+  // ---- block maximum of |x|: wave, then across the four waves
+  uint32_t mb = m2[0] > m2[1] ? m2[0] : m2[1];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off));
+  __shared__ uint32_t wmax[qz::NT / 64];
+  if ((tid & 63) == 0) wmax[tid >> 6] = mb;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < qz::NT / 64; ++w) mb = max(mb, wmax[w]);
+  const float amax = __uint_as_float(mb << 16);
+  const float s = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.f);
+  if (tid == 0) a.scales[sidx] = s;
+
+  // ---- quantise: x / s rounded to fp32, then to e4m3
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int g = i * qz::NT + tid;
+    const int row = g / GPR, col = g % GPR;
+    uint32_t w2[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t p = v[i][2 * half], r = v[i][2 * half + 1];
+      const float f0 = __fdiv_rn(__uint_as_float(p << 16), s);
+      const float f1 = __fdiv_rn(__uint_as_float(p & 0xffff0000u), s);
+      const float f2 = __fdiv_rn(__uint_as_float(r << 16), s);
+      const float f3 = __fdiv_rn(__uint_as_float(r & 0xffff0000u), s);
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, word, true);
+      w2[half] = (uint32_t)word;
+    }
+    if (row < nt) *(u32x2*)(y + row * rs + col * 8) = (u32x2){w2[0], w2[1]};
+  }
+}
+
+template <int D, bool PACKED>
+static hipError_t launch_q(const QuantArgs& a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.nsb * a.H * (PACKED ? 1 : a.B);
+  void* args[] = {const_cast<QuantArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_fp8_kernel<D, PACKED>), dim3((unsigned)grid),
+                         dim3(qz::NT), args, 0, st);
+}
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, int d, bool packed, hipStream_t st) {
+  if (d == 128) return packed ? launch_q<128, true>(a, st) : launch_q<128, false>(a, st);
+  return packed ? launch_q<64, true>(a, st) : launch_q<64, false>(a, st);
+}
+
+int64_t quantize_fp8_grid(int B, int H, int N, bool packed) {
+  const int64_t nb = (N + qz::BLK - 1) / qz::BLK;
+  return packed ? (nb + B) * H : nb * H * B;
+}
+
+}  // namespace iaea

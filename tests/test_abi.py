@@ -26,7 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_status_str", "attn_kernel_name"}
+    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_status_str",
+                                         "attn_kernel_name"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -74,7 +75,8 @@ def test_attn_fwd_rejects(kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(q_scale=None), ia.ATTN_ERR_NULL), (dict(v_scale=None), ia.ATTN_ERR_NULL),
     (dict(o=None), ia.ATTN_ERR_NULL),
-    (dict(d=64), ia.ATTN_ERR_UNSUPPORTED), (dict(cu_seqlens=P), ia.ATTN_ERR_UNSUPPORTED),
+    (dict(d=64), ia.ATTN_ERR_UNSUPPORTED), (dict(cu_seqlens=MIS), ia.ATTN_ERR_ALIGN),
+    (dict(cu_seqlens=P, B=1 << 30, H=4, N=1), ia.ATTN_ERR_SHAPE),
     (dict(causal=-1), ia.ATTN_ERR_UNSUPPORTED),
     (dict(scale=float("-inf")), ia.ATTN_ERR_SCALE),
     (dict(k_scale=MIS), ia.ATTN_ERR_ALIGN), (dict(v=MIS), ia.ATTN_ERR_ALIGN),
@@ -83,6 +85,25 @@ def test_attn_fwd_rejects(kw, status):
 ])
 def test_attn_fwd_fp8_rejects(kw, status):
     assert fp8(**kw) == status
+
+
+def quant(**kw):
+    args = dict(x=P, y=P, scales=P, B=1, H=2, N=300, d=128, cu_seqlens=None, stream=0)
+    args.update(kw)
+    return ia.attn_quantize_fp8(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ia.ATTN_ERR_NULL), (dict(y=None), ia.ATTN_ERR_NULL), (dict(scales=None), ia.ATTN_ERR_NULL),
+    (dict(B=0), ia.ATTN_ERR_SHAPE), (dict(H=0), ia.ATTN_ERR_SHAPE), (dict(N=-5), ia.ATTN_ERR_SHAPE),
+    (dict(B=1 << 16, H=1 << 8, N=1 << 8), ia.ATTN_ERR_SHAPE),
+    (dict(d=96), ia.ATTN_ERR_UNSUPPORTED), (dict(d=256), ia.ATTN_ERR_UNSUPPORTED),
+    (dict(x=MIS), ia.ATTN_ERR_ALIGN), (dict(y=MIS), ia.ATTN_ERR_ALIGN), (dict(scales=MIS), ia.ATTN_ERR_ALIGN),
+    (dict(cu_seqlens=MIS), ia.ATTN_ERR_ALIGN),
+    (dict(cu_seqlens=P, B=1 << 30, H=4, N=1), ia.ATTN_ERR_SHAPE),
+])
+def test_attn_quantize_fp8_rejects(kw, status):
+    assert quant(**kw) == status
 
 
 def test_status_strings():
@@ -95,9 +116,10 @@ def test_status_strings():
 def test_kernel_names():
     assert ia.attn_kernel_name(128, 1, 0, ia.ATTN_BF16) == "attn_fwd_bf16_kernel<d128,causal,fixed,bf16>"
     assert ia.attn_kernel_name(64, 0, 1, ia.ATTN_BF16_OUT_F32) == "attn_fwd_bf16_kernel<d64,full,packed,f32>"
-    assert ia.attn_kernel_name(128, 1, 0, 0, fp8=1) == "attn_fwd_fp8_kernel<causal>"
+    assert ia.attn_kernel_name(128, 1, 0, 0, fp8=1) == "attn_fwd_fp8_kernel<causal,fixed>"
+    assert ia.attn_kernel_name(128, 0, 1, 0, fp8=1) == "attn_fwd_fp8_kernel<full,packed>"
     assert ia.attn_kernel_name(96, 1, 0, 0) == ""
-    assert ia.attn_kernel_name(128, 1, 1, 0, fp8=1) == ""
+    assert ia.attn_kernel_name(64, 1, 1, 0, fp8=1) == ""
     assert ia.attn_kernel_name(128, 3, 0, 0) == ""
 
 
