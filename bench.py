@@ -197,6 +197,140 @@ def cpu_baseline(w, inp, O_gpu, budget_s):
             "seconds": round(dt, 3), "max_abs_err_vs_gpu_on_sample": max_err}
 
 
+def _time_launches(fn, steps, warmup):
+    """Median and mean per-call time (ms) of fn() on the current stream, HIP
+    events around each call, after warmup calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    mean = ev0.elapsed_time(ev1) / steps
+    per = []
+    for _ in range(min(steps, 10)):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        fn()
+        b_.record(stream)
+        b_.synchronize()
+        per.append(a_.elapsed_time(b_))
+    return float(np.median(per)), mean
+
+
+def extra_quantize(args):
+    """bf16 -> e4m3 block quantisation of the fp8 workload's q, k and v
+    ([2, 8192, 16, 128] each), then of the packed workload's layout; an HBM
+    roofline (3 bytes per element plus one fp32 scale per block)."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    import workloads as W
+    w5, w4 = W.workload(5), W.workload(4)
+    dev = torch.device("cuda:0")
+
+    def bf16_dev(seed, shape):
+        b = W.normal_bf16(seed, shape, True)
+        return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    res = {"metric": "bf16 -> e4m3 block quantisation, GB/s of algorithmic HBM traffic", "unit": "GB/s",
+           "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "data": "synthetic (seeded numpy PCG64 bf16 inputs with 1% +-20 outliers)"}
+    out = {}
+    for name, w, packed in (("fixed", w5, False), ("packed", w4, True)):
+        if packed:
+            lengths = W.varlen_lengths(W.tensor_seed(4, "lengths"))
+            cu_h = W.cu_seqlens_from_lengths(lengths)
+            B, N = len(lengths), int(cu_h[-1])
+            shape = (N, w.H, w.d)
+            nsl = (N + 127) // 128 + B
+            sshape = (w.H, nsl)
+            cu = torch.from_numpy(np.asarray(cu_h, np.int32)).to(dev)
+            nblocks = sum(w.H * ((int(L) + 127) // 128) for L in lengths)
+        else:
+            B, N = w.B, w.N
+            shape = (B, N, w.H, w.d)
+            sshape = (B, w.H, (N + 127) // 128)
+            cu = None
+            nblocks = B * w.H * ((N + 127) // 128)
+        xs = [bf16_dev(7000 + i, shape) for i in range(3)]
+        ys = [torch.empty(shape, dtype=torch.uint8, device=dev) for _ in range(3)]
+        ss = [torch.empty(sshape, dtype=torch.float32, device=dev) for _ in range(3)]
+
+        def step():
+            for x, y, sc in zip(xs, ys, ss):
+                ia.attn_quantize_fp8(x, y, sc, B, w.H, N, w.d, cu)
+        med, mean = _time_launches(step, args.steps, args.warmup)
+        elems = int(np.prod(shape))
+        per_launch_bytes = elems * 3 + nblocks * 4
+        t_launch = mean / 3           # back-to-back launches, as the headline line times them
+        out[name] = {"shape": list(shape), "per_step_ms_median": round(med, 5), "per_step_ms_mean": round(mean, 5),
+                     "algorithmic_bytes_per_launch": per_launch_bytes,
+                     "gbps": round(per_launch_bytes / (t_launch * 1e-3) / 1e9, 1)}
+    f = out["fixed"]
+    res["value"] = f["gbps"]
+    res["config"] = {"workload": "quantise q, k, v of fp8_block_scaled_causal_b2_h16_n8192_d128 "
+                                 "(one step = 3 launches)",
+                     "kernel": "quantize_fp8_kernel<128,fixed>", "packed": out["packed"]}
+    res["ms_per_step"] = f["per_step_ms_mean"]
+    res["roofline"] = {"bound": "hbm", "achieved": f["gbps"], "peak": HBM_PEAK, "unit": "GB/s",
+                       "frac": round(f["gbps"] / HBM_PEAK, 4), "traffic": None}
+    # the oracle quantiser on one head of q
+    import oracle.quantize as oq
+    x_h = W.bf16_bits_to_f32(W.normal_bf16(7000, (w5.B, w5.N, w5.H, w5.d), True))[:, :, :1]
+    t0 = time.perf_counter()
+    oq.quantize_blocks(x_h)
+    dt = time.perf_counter() - t0
+    res["cpu_baseline"] = {"value": round(x_h.size * 3 / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                           "kind": "oracle", "sample": f"one head of q ({x_h.size} elements), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
+def extra_fp8_packed(args):
+    """fp8 attention over the packed workload's documents: bf16 q, k, v
+    quantised by attn_quantize_fp8 with document-local scales, then
+    attn_fwd_fp8 with cu_seqlens; only the attention launch is timed."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    import workloads as W
+    w = W.workload(4)
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(w)
+    lengths, cu_h = inp["lengths"], inp["cu_seqlens"]
+    B, N = len(lengths), int(cu_h[-1])
+    cu = torch.from_numpy(np.asarray(cu_h, np.int32)).to(dev)
+    nsl = (N + 127) // 128 + B
+    qkv8, scales = [], []
+    for key in ("q", "k", "v"):
+        x = torch.from_numpy(np.ascontiguousarray(inp[key]).view(np.int16)).view(torch.bfloat16).to(dev)
+        y = torch.empty((N, w.H, w.d), dtype=torch.uint8, device=dev)
+        sc = torch.empty((w.H, nsl), dtype=torch.float32, device=dev)
+        ia.attn_quantize_fp8(x, y, sc, B, w.H, N, w.d, cu)
+        qkv8.append(y)
+        scales.append(sc)
+    o = torch.empty((N, w.H, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.H, N), dtype=torch.float32, device=dev)
+
+    def step():
+        ia.attn_fwd_fp8(*qkv8, *scales, o, lse, B, w.H, N, w.d, w.scale, 1, cu)
+    med, mean = _time_launches(step, args.steps, args.warmup)
+    F = flops(w, lengths)
+    tf = F / (mean * 1e-3) / 1e12
+    res = {"metric": "packed-document fp8 attention fwd TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+           "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(mean, 5), "per_launch_ms_median": round(med, 5), "dtype": "fp8",
+           "data": "synthetic (the packed workload's seeded documents, quantised on the GPU)",
+           "config": {"workload": w.name + " in e4m3 with document-local scales", "documents": B,
+                      "flop_per_step": F, "kernel": ia.attn_kernel_name(w.d, 1, 1, 0, fp8=1)},
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK["fp8"], "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK["fp8"], 4), "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +347,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB (the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--extra", choices=["quantize", "fp8_packed"], default=None,
+                    help="instead of the headline line, time the e4m3 block quantiser or "
+                         "packed-document fp8 attention")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -223,6 +360,13 @@ def main():
     import torch
     import io_aware_exact_attn_amd as ia
     import workloads as W
+
+    if args.extra == "quantize":
+        extra_quantize(args)
+        return
+    if args.extra == "fp8_packed":
+        extra_fp8_packed(args)
+        return
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4

@@ -19,12 +19,20 @@
 //
 // MI355X mapping: the work is a stream through HBM (2 bytes read and 1 written
 // per element), so the kernel is built for bandwidth: one 256-thread
-// workgroup per block, 16-byte loads that cover whole 256-byte token rows, the
+// workgroup per block (two or four blocks per workgroup, with the later
+// blocks' loads issued first, measured slower), 16-byte loads that cover whole 256-byte token rows, the
 // block maximum taken on the bf16 bit patterns (the magnitude order of
 // non-negative floats is the integer order of their bits; v_pk_max_u16 takes
 // two at a time), one wave reduction plus one LDS exchange for the block
-// maximum, the quotient by correctly rounded division, and
-// v_cvt_pk_fp8_f32 for the rounding to e4m3.
+// maximum, and v_cvt_pk_fp8_f32 for the rounding to e4m3.  The quotient x / s
+// needs to be the correctly rounded one; s is the same for the whole block, so
+// one division gives r = RN(1 / s) and each element then takes q0 = RN(x r)
+// and two correction steps q <- RN(q + (x - q s) r), the remainder x - q s
+// exact by fma.  The last step is Markstein's: it returns RN(x / s) when r is
+// within half an ulp of 1 / s and q within one ulp of x / s.  q0 can be 1.5
+// ulp off; after the first step q is within half an ulp plus 2^-24 of one,
+// which the second step needs; the sign is copied from x, so -0 stays -0.
+// Quotients below the fp32 normal range end as e4m3 zero either way.
 #include "attn_common.h"
 #include "attn_kernels.h"
 
@@ -36,25 +44,26 @@ constexpr int NT = 256;    // threads per workgroup
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 }  // namespace qz
 
-template <int D, bool PACKED>
-__global__ void __launch_bounds__(qz::NT) quantize_fp8_kernel(QuantArgs a) {
-  constexpr int GPR = D / 8;                  // 16-byte bf16 granules per token row
-  constexpr int NG = qz::BLK * GPR / qz::NT;  // granules per thread
-  static_assert(NG * qz::NT == qz::BLK * GPR, "block must split evenly over the threads");
+// One work item: block `slot` of head h of sequence b (packed: of the
+// document that owns the slot).  Returns false for a slot no block maps to.
+struct QItem {
+  int64_t base;   // element offset of the block's first token, this head
+  int64_t sidx;   // index of its scale
+  int nt;         // tokens in the block
+};
 
-  // workgroup -> (slot, head, sequence)
-  const int bid = blockIdx.x;
-  const int slot = bid % a.nsb;
-  const int rest = bid / a.nsb;
+template <bool PACKED>
+__device__ __forceinline__ bool q_item(const QuantArgs& a, int item, int D, QItem& it) {
+  const int slot = item % a.nsb;
+  const int rest = item / a.nsb;
   const int h = rest % a.H;
   const int b = rest / a.H;
   int seq_start, seq_len, blk;
-  int64_t sidx;
   if constexpr (!PACKED) {
     blk = slot;
     seq_start = b * a.N;
     seq_len = a.N;
-    sidx = ((int64_t)b * a.H + h) * a.nsb + slot;
+    it.sidx = ((int64_t)b * a.H + h) * a.nsb + slot;
   } else {
     // the document of this slot: the largest doc with cu[doc] / 128 + doc <=
     // slot (that function of doc is strictly increasing)
@@ -67,31 +76,44 @@ __global__ void __launch_bounds__(qz::NT) quantize_fp8_kernel(QuantArgs a) {
     seq_start = a.cu_seqlens[lo];
     seq_len = a.cu_seqlens[lo + 1] - seq_start;
     blk = slot - (seq_start / qz::BLK + lo);
-    if (blk * qz::BLK >= seq_len) return;     // no block maps to this slot
-    sidx = (int64_t)h * a.nsb + slot;
+    if (blk * qz::BLK >= seq_len) return false;
+    it.sidx = (int64_t)h * a.nsb + slot;
   }
   const int t0 = blk * qz::BLK;
-  const int nt = min(qz::BLK, seq_len - t0);   // tokens in this block
-  const int64_t rs = (int64_t)a.H * D;         // elements (and output bytes) between tokens
-  const int64_t base = (int64_t)(seq_start + t0) * rs + (int64_t)h * D;
-  const uint16_t* __restrict__ x = (const uint16_t*)a.x + base;
-  uint8_t* __restrict__ y = (uint8_t*)a.y + base;
+  it.nt = min(qz::BLK, seq_len - t0);
+  it.base = (int64_t)(seq_start + t0) * a.H * D + (int64_t)h * D;
+  return true;
+}
+
+// One workgroup per block: load it, take its maximum, quantise and store.
+template <int D, bool PACKED>
+__global__ void __launch_bounds__(qz::NT) quantize_fp8_kernel(QuantArgs a) {
+  constexpr int GPR = D / 8;                  // 16-byte bf16 granules per token row
+  constexpr int NG = qz::BLK * GPR / qz::NT;  // granules per thread
+  static_assert(NG * qz::NT == qz::BLK * GPR, "block must split evenly over the threads");
   const int tid = threadIdx.x;
+  const int64_t rs = (int64_t)a.H * D;        // elements (and output bytes) between tokens
+  QItem it;
+  if (!q_item<PACKED>(a, blockIdx.x, D, it)) return;   // no block maps to this slot
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x + it.base;
+  uint8_t* __restrict__ y = (uint8_t*)a.y + it.base;
 
   // ---- load the block (a wave covers 64 / GPR whole token rows per step)
   u32x4 v[NG];
-  qz::u16x2 m2 = {0, 0};
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int g = i * qz::NT + tid;
     const int row = g / GPR, col = g % GPR;
-    v[i] = row < nt ? *(const u32x4*)(x + row * rs + col * 8) : (u32x4){0u, 0u, 0u, 0u};
+    v[i] = row < it.nt ? *(const u32x4*)(x + row * rs + col * 8) : (u32x4){0u, 0u, 0u, 0u};
+  }
+
+  // ---- block maximum of |x| on the bit patterns: wave, then workgroup
+  qz::u16x2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < NG; ++i)
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(qz::u16x2, v[i][w] & 0x7fff7fffu));
-  }
-
-  // ---- block maximum of |x|: wave, then across the four waves
   uint32_t mb = m2[0] > m2[1] ? m2[0] : m2[1];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off));
@@ -102,7 +124,14 @@ __global__ void __launch_bounds__(qz::NT) quantize_fp8_kernel(QuantArgs a) {
   for (int w = 0; w < qz::NT / 64; ++w) mb = max(mb, wmax[w]);
   const float amax = __uint_as_float(mb << 16);
   const float s = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.f);
-  if (tid == 0) a.scales[sidx] = s;
+  const float rcp = __fdiv_rn(1.f, s);
+  if (tid == 0) a.scales[it.sidx] = s;
+  auto quot = [&](float xv) __attribute__((always_inline)) {
+    const float q0 = xv * rcp;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, xv), rcp, q0);
+    // x = -0 would come out +0 (the corrections add +0 to -0)
+    return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q1, s, xv), rcp, q1), xv);
+  };
 
   // ---- quantise: x / s rounded to fp32, then to e4m3
 #pragma unroll
@@ -113,15 +142,13 @@ __global__ void __launch_bounds__(qz::NT) quantize_fp8_kernel(QuantArgs a) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const uint32_t p = v[i][2 * half], r = v[i][2 * half + 1];
-      const float f0 = __fdiv_rn(__uint_as_float(p << 16), s);
-      const float f1 = __fdiv_rn(__uint_as_float(p & 0xffff0000u), s);
-      const float f2 = __fdiv_rn(__uint_as_float(r << 16), s);
-      const float f3 = __fdiv_rn(__uint_as_float(r & 0xffff0000u), s);
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, word, true);
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(quot(__uint_as_float(p << 16)),
+                                                 quot(__uint_as_float(p & 0xffff0000u)), 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(quot(__uint_as_float(r << 16)),
+                                             quot(__uint_as_float(r & 0xffff0000u)), word, true);
       w2[half] = (uint32_t)word;
     }
-    if (row < nt) *(u32x2*)(y + row * rs + col * 8) = (u32x2){w2[0], w2[1]};
+    if (row < it.nt) *(u32x2*)(y + row * rs + col * 8) = (u32x2){w2[0], w2[1]};
   }
 }
 

@@ -84,6 +84,22 @@ def test_quantize_packed_bit_exact(d):
     assert np.all(s[:, ~used] == SENTINEL)           # slots no block maps to stay untouched
 
 
+def test_quantize_many_scales_bit_exact():
+    """Every (block, head) gets its own random magnitude 2^u * m (u in
+    [-60, 60], m in [1, 2)), so the blocks' scales, and with them the
+    quotients x / s, cover many different significands."""
+    rng = np.random.default_rng(321)
+    B, N, H, d = 1, 128 * 48, 8, 128
+    x = W.bf16_bits_to_f32(W.normal_bf16(321, (B, N, H, d), True)).astype(np.float64)
+    mag = np.exp2(rng.uniform(-60, 60, (N // 128, H))) * rng.uniform(1, 2, (N // 128, H))
+    x = x * np.repeat(mag, 128, axis=0)[None, :, :, None]
+    bits = W.f32_to_bf16_bits(x.astype(np.float32))
+    y, s = run_quant(bits)
+    yr, sr = oracle_quant(bits)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(y, yr)
+
+
 def test_quantize_workload5_q_tensor():
     """The fp8 workload's shape [2, 8192, 16, 128], every block."""
     w = W.workload(5)
