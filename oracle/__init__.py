@@ -27,12 +27,18 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
                                scale slots, dequantisation error bound; planted
                                mistakes each trip a pin
   quantize.dequantize_blocks   pinned: the dequantisation error bound above
+  backward.attention_grads     pinned (tests/test_backward_oracle.py): central
+                               finite differences (fixed, causal, packed),
+                               torch autograd in float64, closed forms (equal
+                               scores, one key), key-shift invariance; planted
+                               mistakes each trip a pin
+  backward.row_dot             pinned: rowsum(dO * O) = rowsum(P * dP)
 """
 from .exact import (attention, attention_rows, online_softmax_states,
                         e4m3_decode, bf16_decode, dequantize_e4m3_blocks,
                         visible_keys)
-from . import quantize
+from . import backward, quantize
 
 __all__ = ["attention", "attention_rows", "online_softmax_states",
            "e4m3_decode", "bf16_decode", "dequantize_e4m3_blocks", "visible_keys",
-           "quantize"]
+           "backward", "quantize"]
