@@ -47,6 +47,7 @@
  *   attn_fwd_fp8: e4m3 q/k/v with per-128-token block scales, o bf16, d = 128,
  *                 fixed length or packed documents.
  *   attn_quantize_fp8: bf16 -> e4m3 with those block scales, d in {64, 128}.
+ *   attn_bwd:     bf16 gradients of attn_fwd (bf16 output), d in {64, 128}.
  *   Anything else returns an error; there is no fallback path.
  *
  * Ownership and concurrency
@@ -146,6 +147,35 @@ ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
                           const float* q_scale, const float* k_scale, const float* v_scale,
                           void* o, float* lse, int B, int H, int N, int d, float scale,
                           int causal, const int32_t* cu_seqlens, void* stream);
+
+/*
+ * attn_bwd - bf16 exact attention backward: the gradients dQ, dK, dV of
+ * O = softmax(scale * Q K^T + mask) V for an upstream gradient dO, from the
+ * forward's saved LSE (no N x N matrix is stored; probabilities are formed
+ * again tile by tile).  "Flash Attention và IO" asks for the backward pass to
+ * be measured beside the forward when training (section "Kernel đúng còn phải
+ * hợp với tải") and for gradients to be compared across implementations
+ * (section "Bài tập kiểm tính đúng trước khi đo tốc độ"); the pages print no
+ * backward formulas, so the kernels compute the derivative of the forward:
+ *     P_ij = exp(scale q_i . k_j - LSE_i) (0 for a masked key),
+ *     D_i = dO_i . O_i,  dV_j = sum_i P_ij dO_i,
+ *     dS_ij = P_ij (dO_i . v_j - D_i),
+ *     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
+ *   q, k, v     bf16, as given to attn_fwd (same layout, B, H, N, d, scale,
+ *               causal and cu_seqlens).
+ *   o, lse      attn_fwd's bf16 output and fp32 LSE for those inputs.
+ *   dout        bf16 dO, layout of o.
+ *   delta       fp32 workspace with the layout of lse, owned by the caller;
+ *               on return it holds D (rowsum of dO * O).
+ *   dq, dk, dv  bf16 outputs, layout of q; fully overwritten (dq may not alias
+ *               any input).
+ *   d in {64, 128}.  Errors as attn_fwd.  The three kernels are enqueued on
+ *   `stream` in order (D, then dQ, then dK and dV).
+ */
+ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, float* delta, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, float scale, int causal,
+                      const int32_t* cu_seqlens, void* stream);
 
 /*
  * attn_quantize_fp8 - block-scaled e4m3 quantisation of a bf16 tensor, the

@@ -18,7 +18,7 @@ import os
 __all__ = [
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_SCALE",
     "ATTN_ERR_ALIGN", "ATTN_ERR_HIP", "ATTN_BF16", "ATTN_BF16_OUT_F32", "ATTN_FP8_E4M3",
-    "AttnError", "attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_status_str", "attn_kernel_name",
+    "AttnError", "attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_quantize_fp8", "attn_status_str", "attn_kernel_name",
     "library_path", "lib",
 ]
 
@@ -49,6 +49,8 @@ lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _
 lib.attn_fwd.restype = _i
 lib.attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]
 lib.attn_fwd_fp8.restype = _i
+lib.attn_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _vp, _vp]
+lib.attn_bwd.restype = _i
 lib.attn_quantize_fp8.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
 lib.attn_quantize_fp8.restype = _i
 lib.attn_status_str.argtypes = [_i]
@@ -124,4 +126,15 @@ def attn_quantize_fp8(x, y, scales, B, H, N, d, cu_seqlens=None, stream=None, ch
                                _ptr(cu_seqlens), _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_quantize_fp8")
+    return st
+
+
+def attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens=None,
+             stream=None, check: bool = True) -> int:
+    """Enqueue the bf16 attention backward (see ``attn_bwd`` in include/attn.h)."""
+    st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
+                      _ptr(dk), _ptr(dv), int(B), int(H), int(N), int(d), float(scale), int(causal),
+                      _ptr(cu_seqlens), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
     return st

@@ -92,6 +92,34 @@ ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, float* delta, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, float scale, int causal,
+                      const int32_t* cu_seqlens, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * N * H >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if ((int64_t)H * d > ((int64_t)1 << 24)) return ATTN_ERR_SHAPE;
+  for (const void* p : {q, k, v, o, dout, (const void*)lse, (const void*)delta, (const void*)dq,
+                        (const void*)dk, (const void*)dv})
+    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
+  const int64_t bm = iaea::bwd_rows_per_workgroup();
+  if (cu_seqlens && (int64_t)H * ((N + bm - 1) / bm + B) + 8 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  iaea::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.delta = delta;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.cu_seqlens = cu_seqlens;
+  a.B = B; a.H = H; a.N = N;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  const hipError_t e = iaea::launch_attn_bwd(a, d, causal == 1, cu_seqlens != nullptr,
+                                             reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 ATTN_API int attn_quantize_fp8(const void* x, void* y, float* scales, int B, int H, int N, int d,
                                const int32_t* cu_seqlens, void* stream) {
   if (!x || !y || !scales) return ATTN_ERR_NULL;

@@ -1,0 +1,473 @@
+// bf16 exact attention backward for gfx950 (MI355X): dQ, dK, dV.
+//
+// "Flash Attention và IO" asks for the backward pass to be timed beside the
+// forward when the goal is training (section "Kernel đúng còn phải hợp với
+// tải") and its gradients to be compared with another implementation's
+// (section "Bài tập kiểm tính đúng trước khi đo tốc độ").  The pages print no
+// backward algorithm; what is computed is the derivative of the forward, per
+// (sequence, head), with the forward's log-sum-exp L saved instead of the N x N
+// probabilities (the recomputation that keeps the forward IO-aware):
+//     P_ij = exp(scale q_i . k_j - L_i)  (0 for a masked key)
+//     D_i  = dO_i . O_i                   = sum_j P_ij (dO_i . v_j)
+//     dV_j = sum_i P_ij dO_i
+//     dS_ij = P_ij (dO_i . v_j - D_i)
+//     dQ_i = scale sum_j dS_ij k_j,       dK_j = scale sum_i dS_ij q_i.
+// Three kernels, all tile by tile through LDS, nothing N x N in memory:
+//   * delta: D per row, streamed from O and dO;
+//   * dQ: one workgroup per 128 query rows walks the key/value tiles, as the
+//     forward does, with S^T = K Q^T and dP^T = V dO^T and dQ^T += K^T dS^T;
+//   * dK/dV: one workgroup per 128 keys walks the query tiles, with
+//     S = Q K^T and dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS.
+// Splitting dQ from dK/dV recomputes S and dP once more but needs no atomics
+// and no fp32 accumulation buffer for dQ.
+//
+// MI355X mapping: v_mfma_f32_32x32x16_bf16 throughout.  In each kernel the
+// operand that stays (Q and dO, or K and V) lives in VGPRs as the B operand,
+// so every lane owns one row (query or key) of every accumulator; the
+// streamed tiles go from HBM straight to double-buffered, swizzled LDS
+// (buffer_load_dwordx4 ... lds); P and dS are rounded to bf16 and reused as
+// the B operand of the next product in the accumulator's own register order,
+// with the A operand read in the matching order by ds_read_b64_tr_b16.
+#include "attn_common.h"
+#include "attn_kernels.h"
+
+namespace iaea {
+
+namespace bwd {
+constexpr int NW = 4;            // waves per workgroup, 32 rows each
+constexpr int BM = 32 * NW;      // rows (queries or keys) per workgroup
+constexpr int BN = 64;           // rows of a streamed tile
+}  // namespace bwd
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O)
+// ---------------------------------------------------------------------------
+
+template <int D, bool PACKED>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;                   // lanes per row: one 16-byte granule each
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gt / LPR;                // token-head row, (token * H + h)
+  const int g = (int)(gt % LPR);
+  const int64_t rows = (int64_t)(PACKED ? a.N : a.B * a.N) * a.H;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = *((const u32x4*)a.o + row * LPR + g);
+    const u32x4 d = *((const u32x4*)a.dout + row * LPR + g);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = __builtin_fmaf(__uint_as_float(o[w] << 16), __uint_as_float(d[w] << 16), acc);
+      acc = __builtin_fmaf(__uint_as_float(o[w] & 0xffff0000u), __uint_as_float(d[w] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (row < rows && g == 0) {
+    const int64_t token = row / a.H;
+    const int h = (int)(row % a.H);
+    int64_t idx;
+    if constexpr (PACKED) {
+      idx = (int64_t)h * a.N + token;
+    } else {
+      const int64_t b = token / a.N, t = token % a.N;
+      idx = (b * a.H + h) * a.N + t;
+    }
+    a.delta[idx] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// shared pieces of the two gradient kernels
+// ---------------------------------------------------------------------------
+
+// The lane's 8 bf16 of d-chunk dc (B operand, k = d) of row `row` of a [.][H][D]
+// tensor; zero when the row is outside the sequence.
+template <int D>
+__device__ __forceinline__ void load_row_frags(const uint16_t* __restrict__ base, int64_t rs, bool ok,
+                                               int hl, bf16x8 (&f)[D / 16]) {
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) {
+    const u32x4 raw = ok ? *(const u32x4*)(base + dc * 16 + 8 * hl) : (u32x4){0u, 0u, 0u, 0u};
+    f[dc] = __builtin_bit_cast(bf16x8, raw);
+    (void)rs;
+  }
+}
+
+// Stores an accumulator X^T (rows = d, one column per lane: the lane's own row
+// of X) times `mul` as bf16 into row `row` of a [.][H][D] tensor.
+template <int D>
+__device__ __forceinline__ void store_row(uint16_t* __restrict__ dst, const f32x16 (&acc)[D / 32], float mul,
+                                          int hl) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + g * 8 + hl * 4;
+      *(u32x2*)(dst + d) = (u32x2){pack_bf16x2(acc[db][g * 4 + 0] * mul, acc[db][g * 4 + 1] * mul),
+                                   pack_bf16x2(acc[db][g * 4 + 2] * mul, acc[db][g * 4 + 3] * mul)};
+    }
+}
+
+// Packs 16-row chunk ch of a 64-row accumulator pair (two f32x16 of 32 rows)
+// to bf16 in the accumulator's register order: the B operand of the next
+// product, whose A operand is then read with ds_read_tr16 at voff.
+__device__ __forceinline__ bf16x8 pack_chunk(const f32x16 (&x)[2], int ch) {
+  const int kb = ch / 2, c2 = ch % 2;
+  u32x4 w;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(x[kb][8 * c2 + 2 * jj], x[kb][8 * c2 + 2 * jj + 1]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query blocks outer, key/value tiles inner
+// ---------------------------------------------------------------------------
+
+template <int D, bool CAUSAL, bool PACKED>
+__global__ void __launch_bounds__(bwd::NW * 64) bwd_dq_kernel(BwdArgs a) {
+  using namespace bwd;
+  constexpr int ROWB = D * 2, TILE = BN * ROWB;
+  constexpr int CPW = TILE / 1024 / NW;        // 1 KB load chunks per wave per tile
+  constexpr int DC = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
+
+  int h, b, seq_start, seq_len, qblk;
+  if (!decode_work<BM, CAUSAL, PACKED>(a, blockIdx.x, h, b, seq_start, seq_len, qblk)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int q0 = qblk * BM, wq0 = q0 + wave * 32;
+  const int kv_end = CAUSAL ? min(seq_len, q0 + BM) : seq_len;
+  const int n_iter = (kv_end + BN - 1) / BN;
+  const int wave_kv_end = CAUSAL ? min(seq_len, wq0 + 32) : seq_len;
+  const int wave_iters = (wq0 < seq_len) ? (wave_kv_end + BN - 1) / BN : 0;
+  const int64_t rs = (int64_t)a.H * D;
+  const int64_t head_off = (int64_t)h * D;
+  const int64_t lrow = PACKED ? (int64_t)h * a.N + seq_start : (int64_t)(b * a.H + h) * a.N;
+
+  // this lane's query row: Q and dO fragments, L log2(e) and D
+  const int t = wq0 + l32;
+  const bool tok = t < seq_len;
+  const int64_t trow = (int64_t)(seq_start + (tok ? t : 0)) * rs + head_off;
+  bf16x8 qf[DC], df[DC];
+  load_row_frags<D>((const uint16_t*)a.q + trow, rs, tok, hl, qf);
+  load_row_frags<D>((const uint16_t*)a.dout + trow, rs, tok, hl, df);
+  const float lse2 = tok ? a.lse[lrow + t] * kLog2e : 0.f;
+  const float dlt = tok ? a.delta[lrow + t] : 0.f;
+
+  // tile loads
+  uint32_t lane_off[CPW];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    const int byte = (wave * CPW + cc) * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int gr = ((byte % ROWB) >> 4) ^ swz<D>(row);
+    lane_off[cc] = (uint32_t)(((int64_t)row * rs + head_off + gr * 8) * 2);
+  }
+  [[maybe_unused]] const uint32_t row_bytes = (uint32_t)rs * 2u;
+  auto issue_tile = [&](const void* src, int buf, int j) __attribute__((always_inline)) {
+#if __HIP_DEVICE_COMPILE__
+    const int kv0 = j * BN;
+    const uint32_t nrec = (uint32_t)min(seq_len - kv0, BN) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)src + (uint64_t)(uint32_t)(seq_start + kv0) * row_bytes), (short)0, (int)nrec,
+        kBufferFlags);
+    static_for<CPW>([&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (IAEA_LDS void*)(smem + buf * TILE + wave * CPW * 1024),
+                                               16, lane_off[cc] - cc * 1024, 0, cc * 1024, 0);
+    });
+#endif
+  };
+
+  // LDS read offsets: plain fragments (A operand, rows = keys, k = d) and
+  // transposed ones (A operand, rows = d, k = 16 keys in the register order of
+  // the packed chunks)
+  uint32_t koff[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) koff[dc] = l32 * ROWB + (((2 * dc + hl) ^ swz<D>(l32)) << 4);
+  uint32_t voff[2][DB];
+  {
+    const int g16 = lane >> 4;
+    const int v_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+    const int v_dcol = 16 * (g16 & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = v_row + 8 * hi;
+        const int d = db * 32 + v_dcol;
+        voff[hi][db] = row * ROWB + (((d >> 3) ^ swz<D>(row)) << 4) + (d & 7) * 2;
+      }
+  }
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqacc[db] = (f32x16){};
+
+  if (n_iter > 0) {
+    issue_tile(a.k, 0, 0);
+    issue_tile(a.v, 2, 0);
+  }
+  for (int j = 0; j < n_iter; ++j) {
+    const int P = j & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                           // tile j landed; tile j - 1 no longer read
+    if (j + 1 < n_iter) {
+      issue_tile(a.k, P ^ 1, j + 1);
+      issue_tile(a.v, 2 + (P ^ 1), j + 1);
+    }
+    if (j >= wave_iters) continue;
+    const char* kt = smem + P * TILE;
+    const char* vt = smem + (2 + P) * TILE;
+    const int kv0 = j * BN;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 kfr = *(const bf16x8*)(kt + kb * 32 * ROWB + koff[dc]);
+        const bf16x8 vfr = *(const bf16x8*)(vt + kb * 32 * ROWB + koff[dc]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[dc], dc == 0 ? (f32x16){} : s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, df[dc], dc == 0 ? (f32x16){} : dp[kb], 0, 0, 0);
+      }
+    // P^T and dS^T in place; key of register r: kv0 + kb*32 + (r/4)*8 + hl*4 + r%4
+    const bool masked = (kv0 + BN > seq_len) || (CAUSAL && kv0 + BN - 1 > wq0);
+    const int lim = (CAUSAL ? min(t, seq_len - 1) : seq_len - 1) - (kv0 + hl * 4);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -lse2));
+        if (masked && kb * 32 + (r >> 2) * 8 + (r & 3) > lim) p = 0.f;
+        s[kb][r] = p * (dp[kb][r] - dlt);
+      }
+    // dQ^T += K^T dS^T, 16 keys at a time
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 dsf = pack_chunk(s, kc);
+      const char* kk = kt + kc * 16 * ROWB;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x4 lo = ds_read_tr16(kk + voff[0][db]);
+        const bf16x4 hi = ds_read_tr16(kk + voff[1][db]);
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                            dsf, dqacc[db], 0, 0, 0);
+      }
+    }
+  }
+  if (tok) store_row<D>((uint16_t*)a.dq + trow, dqacc, a.scale, hl);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: key blocks outer, query tiles inner
+// ---------------------------------------------------------------------------
+
+template <int D, bool CAUSAL, bool PACKED>
+__global__ void __launch_bounds__(bwd::NW * 64) bwd_dkdv_kernel(BwdArgs a) {
+  using namespace bwd;
+  constexpr int ROWB = D * 2, TILE = BN * ROWB;
+  constexpr int CPW = TILE / 1024 / NW;
+  constexpr int DC = D / 16, DB = D / 32;
+  // Q0 Q1 dO0 dO1, then L log2(e) and D of both tiles (BN floats each)
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 4 * BN * 4];
+  float* lse_t = (float*)(smem + 4 * TILE);    // [2][BN]
+  float* dlt_t = lse_t + 2 * BN;               // [2][BN]
+
+  int h, b, seq_start, seq_len, kblk;
+  // key blocks in natural order: under the causal mask the first blocks see
+  // the most query tiles, so this is longest first
+  if (!decode_work<BM, false, PACKED>(a, blockIdx.x, h, b, seq_start, seq_len, kblk)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int k0 = kblk * BM, wk0 = k0 + wave * 32;
+  const int j_begin = CAUSAL ? k0 / BN : 0;
+  const int j_end = (seq_len + BN - 1) / BN;
+  const int wave_begin = CAUSAL ? wk0 / BN : 0;      // earlier tiles are all masked for this wave
+  const bool wave_live = wk0 < seq_len;
+  const int64_t rs = (int64_t)a.H * D;
+  const int64_t head_off = (int64_t)h * D;
+  [[maybe_unused]] const int64_t lrow = PACKED ? (int64_t)h * a.N + seq_start : (int64_t)(b * a.H + h) * a.N;
+
+  // this lane's key row: K and V fragments
+  const int key = wk0 + l32;
+  const bool kok = key < seq_len;
+  const int64_t krow = (int64_t)(seq_start + (kok ? key : 0)) * rs + head_off;
+  bf16x8 kf[DC], vf[DC];
+  load_row_frags<D>((const uint16_t*)a.k + krow, rs, kok, hl, kf);
+  load_row_frags<D>((const uint16_t*)a.v + krow, rs, kok, hl, vf);
+
+  uint32_t lane_off[CPW];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    const int byte = (wave * CPW + cc) * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int gr = ((byte % ROWB) >> 4) ^ swz<D>(row);
+    lane_off[cc] = (uint32_t)(((int64_t)row * rs + head_off + gr * 8) * 2);
+  }
+  [[maybe_unused]] const uint32_t row_bytes = (uint32_t)rs * 2u;
+  auto issue_tile = [&](int buf, int j) __attribute__((always_inline)) {
+#if __HIP_DEVICE_COMPILE__
+    const int q0 = j * BN;
+    const int nrows = min(seq_len - q0, BN);
+    const uint32_t nrec = (uint32_t)nrows * row_bytes;
+    const uint64_t off = (uint64_t)(uint32_t)(seq_start + q0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)a.q + off), (short)0, (int)nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)a.dout + off), (short)0, (int)nrec, kBufferFlags);
+    static_for<CPW>([&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (IAEA_LDS void*)(smem + buf * TILE + wave * CPW * 1024),
+                                               16, lane_off[cc] - cc * 1024, 0, cc * 1024, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (IAEA_LDS void*)(smem + (2 + buf) * TILE + wave * CPW * 1024),
+                                               16, lane_off[cc] - cc * 1024, 0, cc * 1024, 0);
+    });
+    // the tile's L and D: one dword per lane (rows past the end read as 0)
+    if (wave < 2) {
+      const float* src = wave == 0 ? a.lse : a.delta;
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(src + lrow + q0), (short)0, nrows * 4, kBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (IAEA_LDS void*)((wave == 0 ? lse_t : dlt_t) + buf * BN),
+                                               4, lane * 4, 0, 0, 0);
+    }
+#endif
+  };
+
+  uint32_t qoff[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) qoff[dc] = l32 * ROWB + (((2 * dc + hl) ^ swz<D>(l32)) << 4);
+  uint32_t voff[2][DB];
+  {
+    const int g16 = lane >> 4;
+    const int v_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+    const int v_dcol = 16 * (g16 & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = v_row + 8 * hi;
+        const int d = db * 32 + v_dcol;
+        voff[hi][db] = row * ROWB + (((d >> 3) ^ swz<D>(row)) << 4) + (d & 7) * 2;
+      }
+  }
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dkacc[db] = dvacc[db] = (f32x16){};
+
+  if (j_begin < j_end) issue_tile(0, j_begin);
+  for (int j = j_begin; j < j_end; ++j) {
+    const int P = (j - j_begin) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < j_end) issue_tile(P ^ 1, j + 1);
+    if (!wave_live || j < wave_begin) continue;
+    const char* qt = smem + P * TILE;
+    const char* dt = smem + (2 + P) * TILE;
+    const int q0 = j * BN;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 qfr = *(const bf16x8*)(qt + qb * 32 * ROWB + qoff[dc]);
+        const bf16x8 dfr = *(const bf16x8*)(dt + qb * 32 * ROWB + qoff[dc]);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr, kf[dc], dc == 0 ? (f32x16){} : s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp[qb], 0, 0, 0);
+      }
+    // query of register r: q0 + qb*32 + (r/4)*8 + hl*4 + r%4; its L and D
+    // come from the tile's LDS rows, four at a time
+    const bool masked = (q0 + BN > seq_len) || (wk0 + 32 > seq_len) || (CAUSAL && q0 < wk0 + 31);
+    f32x16 pp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = qb * 32 + g * 8 + hl * 4;
+        const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
+        const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = g * 4 + i;
+          float p = fast_exp2(__builtin_fmaf(s[qb][r], a.c, -l4[i] * kLog2e));
+          if (masked) {
+            const int qrow = q0 + qi + i;
+            if (qrow >= seq_len || !kok || (CAUSAL && key > qrow)) p = 0.f;
+          }
+          pp[qb][r] = p;
+          s[qb][r] = p * (dp[qb][r] - d4[i]);
+        }
+      }
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 pf = pack_chunk(pp, kc);
+      const bf16x8 dsf = pack_chunk(s, kc);
+      const char* dd = dt + kc * 16 * ROWB;
+      const char* qq = qt + kc * 16 * ROWB;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x4 dlo = ds_read_tr16(dd + voff[0][db]);
+        const bf16x4 dhi = ds_read_tr16(dd + voff[1][db]);
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                            pf, dvacc[db], 0, 0, 0);
+        const bf16x4 qlo = ds_read_tr16(qq + voff[0][db]);
+        const bf16x4 qhi = ds_read_tr16(qq + voff[1][db]);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                            dsf, dkacc[db], 0, 0, 0);
+      }
+    }
+  }
+  if (kok) {
+    store_row<D>((uint16_t*)a.dk + krow, dkacc, a.scale, hl);
+    store_row<D>((uint16_t*)a.dv + krow, dvacc, 1.f, hl);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+
+template <int D, bool CAUSAL, bool PACKED>
+static hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
+  constexpr int BM = bwd::BM;
+  {
+    const int64_t rows = (int64_t)(PACKED ? a.N : a.B * a.N) * a.H;
+    const int64_t grid = (rows * (D / 8) + 255) / 256;
+    void* args[] = {&a};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_delta_kernel<D, PACKED>),
+                                         dim3((unsigned)grid), dim3(256), args, 0, st);
+    if (e != hipSuccess) return e;
+  }
+  if (PACKED) {
+    a.slots = (a.N + BM - 1) / BM + a.B;
+    a.n_work = a.H * a.slots;
+  } else {
+    a.slots = (a.N + BM - 1) / BM;
+    a.n_work = a.B * a.H * a.slots;
+  }
+  const int grid = (a.n_work + kXcds - 1) / kXcds * kXcds;
+  a.per_xcd = grid / kXcds;
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<D, CAUSAL, PACKED>), dim3(grid),
+                                 dim3(bwd::NW * 64), args, 0, st);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, PACKED>), dim3(grid),
+                         dim3(bwd::NW * 64), args, 0, st);
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, bool packed, hipStream_t st) {
+  if (packed) return causal ? launch_bwd_t<D, true, true>(a, st) : launch_bwd_t<D, false, true>(a, st);
+  return causal ? launch_bwd_t<D, true, false>(a, st) : launch_bwd_t<D, false, false>(a, st);
+}
+
+hipError_t launch_attn_bwd(const BwdArgs& a, int d, bool causal, bool packed, hipStream_t st) {
+  return d == 128 ? launch_bwd_d<128>(a, causal, packed, st) : launch_bwd_d<64>(a, causal, packed, st);
+}
+
+int bwd_rows_per_workgroup() { return bwd::BM; }
+
+}  // namespace iaea

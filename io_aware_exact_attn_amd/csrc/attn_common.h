@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace iaea {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -50,6 +52,27 @@ struct FwdArgs {
   float lse_mul;             // ln 2: LSE = ln2 * (m_scaled + log2 l)
 };
 
+// Arguments of the backward kernels.
+struct BwdArgs {
+  const void* q;             // bf16 [B][N][H][d] (packed [N][H][d]), as the forward
+  const void* k;
+  const void* v;
+  const void* o;             // the forward's output
+  const void* dout;          // upstream gradient dO, layout of o
+  const float* lse;          // the forward's LSE, [B][H][N] (packed [H][N])
+  float* delta;              // D = rowsum(dO * O), layout of lse (written, then read)
+  void* dq;                  // bf16 outputs, layout of q
+  void* dk;
+  void* dv;
+  const int32_t* cu_seqlens; // packed documents, device, B + 1 entries
+  int B, H, N;
+  int slots;                 // workgroup slots per head (packed) or blocks per sequence
+  int n_work;                // number of real work items
+  int per_xcd;               // grid / 8
+  float scale;               // the forward's scale (any sign)
+  float c;                   // scale * log2(e)
+};
+
 // Arguments of the e4m3 block quantiser.
 struct QuantArgs {
   const void* x;             // bf16 input, [B][N][H][d] or packed [N][H][d]
@@ -59,6 +82,34 @@ struct QuantArgs {
   int B, H, N;
   int nsb;                   // scale slots per (sequence, head): ceil(N / 128), packed + B
 };
+
+// 16-byte-granule XOR swizzle of a bf16 LDS row of D elements: conflict-free
+// for the MFMA fragment reads along rows (16 consecutive rows, one granule)
+// and for the transposed reads (ds_read_b64_tr_b16) of the bf16 kernels.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// The restrict-qualified pointer gives the read alias-scope metadata; without
+// it the compiler cannot tell it from the in-flight LDS DMA of other buffers
+// and waits for every outstanding tile load before it.
+__device__ __forceinline__ bf16x4 ds_read_tr16(const char* __restrict__ p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IAEA_LDS s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Calls f(integral_constant<int, I>) for I = 0 .. N - 1, fully unrolled, so
+// register arrays are indexed by compile-time constants.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Undo the round-robin XCD dispatch: consecutive logical indices land on one
 // XCD, so workgroups that run together on an XCD share its L2 (packed
@@ -86,8 +137,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // schedules longest first and the last ones to start are the shortest.  The
 // (sequence, head) index is the minor one: the round-robin over the 8 XCDs
 // then keeps each (sequence, head) on one XCD when B H is a multiple of 8.
-template <int BM, bool CAUSAL, bool PACKED>
-__device__ __forceinline__ bool decode_work(const FwdArgs& a, int bid, int& h, int& b,
+template <int BM, bool CAUSAL, bool PACKED, class Args>
+__device__ __forceinline__ bool decode_work(const Args& a, int bid, int& h, int& b,
                                             int& seq_start, int& seq_len, int& qblk) {
   if constexpr (!PACKED) {
     const int lb = bid;

@@ -35,35 +35,8 @@
 #include "attn_common.h"
 #include "attn_kernels.h"
 
-#include <utility>
 
 namespace iaea {
-
-// 16-byte-granule XOR swizzle of an LDS row (see the file comment).
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-// The restrict-qualified pointer gives the read alias-scope metadata; without
-// it the compiler cannot tell it from the in-flight LDS DMA of other buffers
-// and waits for every outstanding tile load before it.
-__device__ __forceinline__ bf16x4 ds_read_tr16(const char* __restrict__ p) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IAEA_LDS s16x4*)(p));
-  return __builtin_bit_cast(bf16x4, r);
-}
-
-// Calls f(integral_constant<int, I>) for I = 0 .. N - 1, fully unrolled, so
-// register arrays are indexed by compile-time constants.
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 template <int P> using Parity = std::integral_constant<int, P>;
 

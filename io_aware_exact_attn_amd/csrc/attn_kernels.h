@@ -15,6 +15,11 @@ int bf16_rows_per_workgroup(int d);
 // packed documents (document-local scale blocks).
 hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool causal, bool packed, hipStream_t st);
 
+// bf16 backward: D = rowsum(dO * O) into a.delta, then dQ, then dK and dV;
+// d in {64, 128}.  Arguments already validated.
+hipError_t launch_attn_bwd(const BwdArgs& a, int d, bool causal, bool packed, hipStream_t st);
+int bwd_rows_per_workgroup();
+
 // bf16 -> e4m3 with per-128-token block scales; d in {64, 128}.
 hipError_t launch_quantize_fp8(const QuantArgs& a, int d, bool packed, hipStream_t st);
 int64_t quantize_fp8_grid(int B, int H, int N, bool packed);

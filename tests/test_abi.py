@@ -26,8 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_status_str",
-                                         "attn_kernel_name"}
+    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_bwd",
+                                         "attn_status_str", "attn_kernel_name"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -104,6 +104,30 @@ def quant(**kw):
 ])
 def test_attn_quantize_fp8_rejects(kw, status):
     assert quant(**kw) == status
+
+
+def bwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, delta=P, dq=P, dk=P, dv=P, B=1, H=2, N=300, d=128,
+                scale=0.1, causal=1, cu_seqlens=None, stream=0)
+    args.update(kw)
+    return ia.attn_bwd(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ia.ATTN_ERR_NULL), (dict(dout=None), ia.ATTN_ERR_NULL), (dict(lse=None), ia.ATTN_ERR_NULL),
+    (dict(delta=None), ia.ATTN_ERR_NULL), (dict(dq=None), ia.ATTN_ERR_NULL), (dict(dv=None), ia.ATTN_ERR_NULL),
+    (dict(B=0), ia.ATTN_ERR_SHAPE), (dict(H=0), ia.ATTN_ERR_SHAPE), (dict(N=-1), ia.ATTN_ERR_SHAPE),
+    (dict(B=1 << 16, H=1 << 8, N=1 << 8), ia.ATTN_ERR_SHAPE),
+    (dict(d=96), ia.ATTN_ERR_UNSUPPORTED), (dict(d=256), ia.ATTN_ERR_UNSUPPORTED),
+    (dict(causal=2), ia.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), ia.ATTN_ERR_SCALE),
+    (dict(o=MIS), ia.ATTN_ERR_ALIGN), (dict(delta=MIS), ia.ATTN_ERR_ALIGN), (dict(dk=MIS), ia.ATTN_ERR_ALIGN),
+    (dict(cu_seqlens=MIS), ia.ATTN_ERR_ALIGN),
+    (dict(cu_seqlens=P, B=1 << 30, H=4, N=1), ia.ATTN_ERR_SHAPE),
+    (dict(H=(1 << 17) + 1, N=1), ia.ATTN_ERR_SHAPE),     # H * d > 2^24
+])
+def test_attn_bwd_rejects(kw, status):
+    assert bwd(**kw) == status
 
 
 def test_status_strings():

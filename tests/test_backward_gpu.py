@@ -1,0 +1,191 @@
+"""GPU parity of the attention backward (attn_bwd) against the fp64 gradient
+oracle (oracle.backward), on the same seeded bf16 inputs, with O and the LSE
+taken from the HIP forward (attn_fwd) as a training step would.
+
+Tolerance, derived from the arithmetic of the kernels rather than fixed:
+every input (Q, K, V, dO) is bf16 on both sides, so the kernels' errors come
+from
+  * P: the forward's LSE is the log of a sum of bf16-rounded probabilities
+    (relative error of the sum <= 2^-9), and the backward rounds P to bf16
+    before dV = P^T dO (another 2^-9): |P~ - P| <= 2^-8 P to first order;
+    2^-7 P is allowed;
+  * D = rowsum(dO * O) is taken from the forward's bf16 O, so
+    |D~ - D| <= sum_d |dO| |O~ - O| with O~ the HIP output;
+  * dS = P (dP - D) is rounded to bf16 (2^-9 |dS|) before dQ and dK;
+  * the fp32 sums of d products behind S, dP and D, each within 2^-18 of its
+    sum of absolute products (the worst case of a 128-term fp32 sum is
+    2^-17; its typical error is 2^-20): this is what is left of dP - D when
+    one key holds all the weight and the two nearly cancel, and it moves P
+    by a relative |scale| 2^-18 (|q_i| . |k_j| + max_j' |q_i| . |k_j'|);
+  * the bf16 output rounding, half an ulp of the result.
+Propagated without cancellation, element by element:
+    |dV~ - dV| <= (2^-7 + e_S) (P^T |dO|)                + half ulp
+    E = (2^-7 + e_S) P |dP - D| + P (|D~ - D| + 2^-18 (|dO| |V|^T + |dO| . |O|)) + 2^-9 |dS|
+    |dQ~ - dQ| <= |scale| E |K|,  |dK~ - dK| <= |scale| E^T |Q|  (+ half ulp)
+That is a worst case (all errors of one sign); the Frobenius error of each
+gradient relative to its norm must also stay below 2^-7, which a
+systematic mistake (a dropped mask, a wrong row term) exceeds.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.backward as ob
+import workloads as W
+from parity import bf16_half_ulp, oracle_bf16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+REL_P = 2.0 ** -7
+REL_DS = 2.0 ** -9
+REL_SUM = 2.0 ** -18
+ABS_FLOOR = 1e-5
+
+
+def _inputs(seed, shape):
+    return tuple(W.normal_bf16(seed * 10 + i, shape) for i in range(4))   # q, k, v, dO
+
+
+def run_fwd_bwd(q, k, v, do, scale, causal, cu=None):
+    """Forward then backward through the C ABI.  Returns float64 arrays
+    (O, dQ, dK, dV, delta) in the input layouts, delta laid out as the LSE."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    packed = cu is not None
+    if packed:
+        N, H, d = q.shape
+        B = len(cu) - 1
+        lshape = (H, N)
+    else:
+        B, N, H, d = q.shape
+        lshape = (B, H, N)
+    tq, tk, tv, tdo = (to_dev(x) for x in (q, k, v, do))
+    o = torch.full(q.shape, 77.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(lshape, 77.0, dtype=torch.float32, device="cuda")
+    cud = to_dev(np.asarray(cu, np.int32)) if packed else None
+    ia.attn_fwd(tq, tk, tv, o, lse, B, H, N, d, scale, int(causal), cud, ia.ATTN_BF16)
+    delta = torch.full(lshape, 77.0, dtype=torch.float32, device="cuda")
+    g = [torch.full(q.shape, 77.0, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    ia.attn_bwd(tq, tk, tv, o, tdo, lse, delta, g[0], g[1], g[2], B, H, N, d, scale, int(causal), cud)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    return f(o), f(g[0]), f(g[1]), f(g[2]), f(delta)
+
+
+def _seq_bounds(q, k, v, do, o_gpu, o_ref, scale, causal):
+    """Per-element bounds of one (sequence, head), from fp64 quantities."""
+    n = q.shape[0]
+    s = scale * (q @ k.T)
+    if causal:
+        s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    p /= p.sum(axis=1, keepdims=True)
+    dp = do @ v.T
+    dd = (o_ref * do).sum(axis=1, keepdims=True)
+    err_d = (np.abs(do) * np.abs(o_gpu - o_ref)).sum(axis=1, keepdims=True)
+    ds = p * (dp - dd)
+    qk = np.abs(q) @ np.abs(k).T
+    rel = REL_P + abs(scale) * REL_SUM * (qk + qk.max(axis=1, keepdims=True))
+    sums = REL_SUM * (np.abs(do) @ np.abs(v).T + (np.abs(do) * np.abs(o_ref)).sum(axis=1, keepdims=True))
+    e = rel * p * np.abs(dp - dd) + p * (err_d + sums) + REL_DS * np.abs(ds)
+    bq = abs(scale) * (e @ np.abs(k))
+    bk = abs(scale) * (e.T @ np.abs(q))
+    bv = (rel * p).T @ np.abs(do)
+    return bq, bk, bv
+
+
+def _bounds(q, k, v, do, o_gpu, o_ref, scale, causal, cu=None):
+    out = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)]
+    if cu is not None:
+        for a, b in zip(cu[:-1], cu[1:]):
+            if b <= a:
+                continue
+            for h in range(q.shape[1]):
+                r = _seq_bounds(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], o_gpu[a:b, h], o_ref[a:b, h],
+                                scale, causal)
+                for x, y in zip(out, r):
+                    x[a:b, h] = y
+        return out
+    for bb in range(q.shape[0]):
+        for h in range(q.shape[2]):
+            r = _seq_bounds(q[bb, :, h], k[bb, :, h], v[bb, :, h], do[bb, :, h], o_gpu[bb, :, h],
+                            o_ref[bb, :, h], scale, causal)
+            for x, y in zip(out, r):
+                x[bb, :, h] = y
+    return out
+
+
+def check_case(bits, scale, causal, cu=None):
+    q, k, v, do = bits
+    O, dq, dk, dv, delta = run_fwd_bwd(q, k, v, do, scale, causal, cu)
+    qf, kf, vf, dof = (oracle.bf16_decode(x) for x in bits)
+    Or, _ = oracle_bf16(q, k, v, scale, causal, cu_seqlens=cu)
+    want = ob.attention_grads(qf, kf, vf, dof, scale, causal, cu)
+    bounds = _bounds(qf, kf, vf, dof, O, Or, scale, causal, cu)
+    report = {}
+    for name, got, ref, bnd in zip(("dq", "dk", "dv"), (dq, dk, dv), want, bounds):
+        assert np.all(np.isfinite(got)), name
+        err = np.abs(got - ref)
+        lim = bnd + bf16_half_ulp(np.maximum(np.abs(got), np.abs(ref))) + ABS_FLOOR
+        worst = float((err / lim).max()) if err.size else 0.0
+        nref = float(np.linalg.norm(ref))
+        rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got))
+        report[name] = dict(max_abs=float(err.max()) if err.size else 0.0, worst_ratio=worst, frob_rel=rel)
+        assert worst <= 1.0, (name, report)
+        assert rel <= REL_P, (name, report)
+    # D against rowsum(dO * O) of the O the kernel was given (fp32 sums of
+    # exact bf16 products)
+    dref = ob.row_dot(O, dof)
+    dabs = ob.row_dot(np.abs(O), np.abs(dof))
+    assert np.all(np.abs(delta - dref) <= 1e-5 * dabs + 1e-30), "delta"
+    return report
+
+
+FIXED = [(1, 2, 1, 128), (2, 2, 63, 64), (1, 2, 64, 128), (2, 1, 65, 64), (1, 2, 127, 128),
+         (1, 2, 129, 64), (1, 2, 300, 128), (1, 1, 1000, 64), (1, 1, 1000, 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d", FIXED)
+def test_bwd_fixed(B, H, N, d, causal):
+    bits = _inputs(1000 + N + d, (B, N, H, d))
+    check_case(bits, 1.0 / np.sqrt(d), causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_packed(d, causal):
+    lengths = [1, 127, 0, 128, 129, 300, 513, 64, 0, 255]
+    cu = W.cu_seqlens_from_lengths(lengths)
+    bits = _inputs(2000 + d, (int(cu[-1]), 2, d))
+    check_case(bits, 1.0 / np.sqrt(d), causal, [int(x) for x in cu])
+
+
+def test_bwd_packed_many_documents():
+    """More than 64 documents: the work decode's other branch."""
+    rng = np.random.default_rng(5)
+    lengths = [int(x) for x in rng.integers(0, 90, size=80)]
+    cu = W.cu_seqlens_from_lengths(lengths)
+    bits = _inputs(2100, (int(cu[-1]), 2, 128))
+    check_case(bits, 0.088, True, [int(x) for x in cu])
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5])
+def test_bwd_scales(scale):
+    """A negative scale (the order of the scores flips), zero (uniform P, so
+    dQ = dK = 0 exactly) and a large one (peaked P)."""
+    bits = _inputs(3000, (1, 200, 2, 128))
+    check_case(bits, scale, True)
+    if scale == 0.0:
+        q, k, v, do = bits
+        _, dq, dk, _, _ = run_fwd_bwd(q, k, v, do, scale, True)
+        assert np.all(dq == 0) and np.all(dk == 0)
+
+
+def test_bwd_gradient_outliers():
+    """Keys with +-20 outliers: peaked rows and large |dP - D|."""
+    shape = (1, 257, 2, 128)
+    q, k, v = (W.normal_bf16(4000 + i, shape, outliers=True) for i in range(3))
+    do = W.normal_bf16(4003, shape)
+    check_case((q, k, v, do), 1.0 / np.sqrt(128), True)
