@@ -331,6 +331,87 @@ def extra_fp8_packed(args):
     print(json.dumps(res), flush=True)
 
 
+def extra_bwd(args):
+    """The bf16 attention backward (attn_bwd: delta, dQ and dK/dV launches) on
+    a bf16 workload, with O and the LSE from attn_fwd and a seeded dO.
+    Throughput counts the backward's five N^2 d products (S recomputed, dP,
+    dV, dQ, dK) at 2 flops each: 2.5 times the forward's dense count, halved
+    for causal masking.  The kernels themselves recompute S and dP once more
+    (in the dQ kernel and in the dK/dV kernel), so they issue 7/5 of that."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    import workloads as W
+    w = W.workload(args.workload)
+    if w.fp8:
+        raise SystemExit("the backward is bf16: pick a bf16 workload")
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(w)
+
+    def td(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = td(inp["q"]), td(inp["k"]), td(inp["v"])
+    if w.varlen:
+        lengths = inp["lengths"]
+        B, N = len(lengths), w.N
+        lse_shape = (w.H, N)
+        cu = torch.from_numpy(np.asarray(inp["cu_seqlens"], np.int32)).to(dev)
+    else:
+        lengths = None
+        B, N = w.B, w.N
+        lse_shape = (B, w.H, N)
+        cu = None
+    do_bits = W.normal_bf16(W.tensor_seed(w.cid, "q") + 500, tuple(q.shape))
+    do = td(do_bits)
+    o = torch.empty_like(q)
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+    ia.attn_fwd(q, k, v, o, lse, B, w.H, N, w.d, w.scale, int(w.causal), cu, ia.ATTN_BF16)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ia.attn_bwd(q, k, v, o, do, lse, delta, dq, dk, dv, B, w.H, N, w.d, w.scale, int(w.causal), cu,
+                    stream)
+    med, mean = _time_launches(step, args.steps, args.warmup)
+    F = 2.5 * flops(w, lengths)
+    tf = F / (mean * 1e-3) / 1e12
+    res = {"metric": "attention bwd TFLOP/s (dQ, dK, dV; 2.5x the forward's dense count)",
+           "value": round(tf, 2), "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(mean, 5),
+           "per_step_ms_median": round(med, 5), "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (the workload's seeded q, k, v; dO seeded N(0,1) bf16)",
+           "config": {"workload": w.name + " backward", "B": B, "H": w.H, "N": N, "d": w.d,
+                      "causal": w.causal, "packed": w.varlen, "flop_per_step": F,
+                      "kernels": ["bwd_delta_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]},
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK["bf16"], "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK["bf16"], 4), "traffic": None,
+                        "note": "whole step (three launches); per-kernel times from rocprofv3"}}
+    if not args.no_cpu_baseline:
+        import oracle
+        import oracle.backward as ob
+        qd, kd, vd = (oracle.bf16_decode(inp[t]) for t in ("q", "k", "v"))
+        dod = oracle.bf16_decode(do_bits)
+        t0 = time.perf_counter()
+        if w.varlen:
+            sl = (slice(None), slice(0, 1))
+            ob.attention_grads(qd[sl], kd[sl], vd[sl], dod[sl], w.scale, w.causal, inp["cu_seqlens"])
+        else:
+            sl = (slice(0, 1), slice(None), slice(0, 1))
+            ob.attention_grads(qd[sl], kd[sl], vd[sl], dod[sl], w.scale, w.causal)
+        dt = time.perf_counter() - t0
+        fh = F / (w.H * (1 if w.varlen else B))
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        except Exception:
+            cores = os.cpu_count()
+        res["cpu_baseline"] = {"value": fh / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                               "sample": f"one (sequence, head) of the workload, fp64 numpy gradient "
+                                         f"oracle; {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,9 +428,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB (the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--extra", choices=["quantize", "fp8_packed"], default=None,
-                    help="instead of the headline line, time the e4m3 block quantiser or "
-                         "packed-document fp8 attention")
+    ap.add_argument("--extra", choices=["quantize", "fp8_packed", "bwd"], default=None,
+                    help="instead of the headline line, time the e4m3 block quantiser, "
+                         "packed-document fp8 attention or the bf16 backward (on --workload)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -366,6 +447,9 @@ def main():
         return
     if args.extra == "fp8_packed":
         extra_fp8_packed(args)
+        return
+    if args.extra == "bwd":
+        extra_bwd(args)
         return
 
     if args.copy_calibration:
