@@ -367,22 +367,24 @@ __global__ void __launch_bounds__(bwd::NW * 64) bwd_dkdv_kernel(BwdArgs a) {
     const char* qt = smem + P * TILE;
     const char* dt = smem + (2 + P) * TILE;
     const int q0 = j * BN;
-    f32x16 s[2], dp[2];
+    // visible queries of this lane's key, as offsets in the tile: [lo, hi]
+    const int lo = CAUSAL ? key - q0 : 0;
+    const int hi = kok ? seq_len - 1 - q0 : -1;
+    // the tile in two halves of 32 queries: S and dP of a half, then its
+    // products into dV and dK, so only one half's scores are live at a time
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb) {
+      __builtin_amdgcn_sched_barrier(0);       // keep each half's loads inside the half
+      f32x16 s, dp;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const bf16x8 qfr = *(const bf16x8*)(qt + qb * 32 * ROWB + qoff[dc]);
         const bf16x8 dfr = *(const bf16x8*)(dt + qb * 32 * ROWB + qoff[dc]);
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr, kf[dc], dc == 0 ? (f32x16){} : s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp[qb], 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr, kf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
       }
-    // query of register r: q0 + qb*32 + (r/4)*8 + hl*4 + r%4; its L and D
-    // come from the tile's LDS rows, four at a time
-    const bool masked = (q0 + BN > seq_len) || (wk0 + 32 > seq_len) || (CAUSAL && q0 < wk0 + 31);
-    f32x16 pp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      // query of register r: q0 + qb*32 + (r/4)*8 + hl*4 + r%4; its L and D
+      // come from the tile's LDS rows, four at a time.  P goes to s, dS to dp.
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qi = qb * 32 + g * 8 + hl * 4;
@@ -391,32 +393,37 @@ __global__ void __launch_bounds__(bwd::NW * 64) bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = g * 4 + i;
-          float p = fast_exp2(__builtin_fmaf(s[qb][r], a.c, -l4[i] * kLog2e));
-          if (masked) {
-            const int qrow = q0 + qi + i;
-            if (qrow >= seq_len || !kok || (CAUSAL && key > qrow)) p = 0.f;
-          }
-          pp[qb][r] = p;
-          s[qb][r] = p * (dp[qb][r] - d4[i]);
+          float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
+          if (qi + i < lo || qi + i > hi) p = 0.f;
+          s[r] = p;
+          dp[r] = p * (dp[r] - d4[i]);
         }
       }
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time
+      // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const bf16x8 pf = pack_chunk(pp, kc);
-      const bf16x8 dsf = pack_chunk(s, kc);
-      const char* dd = dt + kc * 16 * ROWB;
-      const char* qq = qt + kc * 16 * ROWB;
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 pw, dw;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x4 dlo = ds_read_tr16(dd + voff[0][db]);
-        const bf16x4 dhi = ds_read_tr16(dd + voff[1][db]);
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                            pf, dvacc[db], 0, 0, 0);
-        const bf16x4 qlo = ds_read_tr16(qq + voff[0][db]);
-        const bf16x4 qhi = ds_read_tr16(qq + voff[1][db]);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                            dsf, dkacc[db], 0, 0, 0);
+        for (int jj = 0; jj < 4; ++jj) {
+          pw[jj] = pack_bf16x2(s[8 * c2 + 2 * jj], s[8 * c2 + 2 * jj + 1]);
+          dw[jj] = pack_bf16x2(dp[8 * c2 + 2 * jj], dp[8 * c2 + 2 * jj + 1]);
+        }
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+        const bf16x8 dsf = __builtin_bit_cast(bf16x8, dw);
+        const int kc = qb * 2 + c2;
+        const char* dd = dt + kc * 16 * ROWB;
+        const char* qq = qt + kc * 16 * ROWB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x4 dlo = ds_read_tr16(dd + voff[0][db]);
+          const bf16x4 dhi = ds_read_tr16(dd + voff[1][db]);
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                              pf, dvacc[db], 0, 0, 0);
+          const bf16x4 qlo = ds_read_tr16(qq + voff[0][db]);
+          const bf16x4 qhi = ds_read_tr16(qq + voff[1][db]);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                              dsf, dkacc[db], 0, 0, 0);
+        }
       }
     }
   }
