@@ -108,23 +108,13 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ dst, const f32x
     }
 }
 
-// Packs 16-row chunk ch of a 64-row accumulator pair (two f32x16 of 32 rows)
-// to bf16 in the accumulator's register order: the B operand of the next
-// product, whose A operand is then read with ds_read_tr16 at voff.
-__device__ __forceinline__ bf16x8 pack_chunk(const f32x16 (&x)[2], int ch) {
-  const int kb = ch / 2, c2 = ch % 2;
-  u32x4 w;
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(x[kb][8 * c2 + 2 * jj], x[kb][8 * c2 + 2 * jj + 1]);
-  return __builtin_bit_cast(bf16x8, w);
-}
-
 // ---------------------------------------------------------------------------
 // dQ: query blocks outer, key/value tiles inner
 // ---------------------------------------------------------------------------
 
 template <int D, bool CAUSAL, bool PACKED>
-__global__ void __launch_bounds__(bwd::NW * 64) bwd_dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(bwd::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq_kernel(BwdArgs a) {
   using namespace bwd;
   constexpr int ROWB = D * 2, TILE = BN * ROWB;
   constexpr int CPW = TILE / 1024 / NW;        // 1 KB load chunks per wave per tile
@@ -221,38 +211,41 @@ __global__ void __launch_bounds__(bwd::NW * 64) bwd_dq_kernel(BwdArgs a) {
     const char* kt = smem + P * TILE;
     const char* vt = smem + (2 + P) * TILE;
     const int kv0 = j * BN;
-    f32x16 s[2], dp[2];
+    // the tile in two halves of 32 keys: S^T and dP^T of a half, then its
+    // product into dQ^T
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const bf16x8 kfr = *(const bf16x8*)(kt + kb * 32 * ROWB + koff[dc]);
         const bf16x8 vfr = *(const bf16x8*)(vt + kb * 32 * ROWB + koff[dc]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[dc], dc == 0 ? (f32x16){} : s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, df[dc], dc == 0 ? (f32x16){} : dp[kb], 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, df[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
       }
-    // P^T and dS^T in place; key of register r: kv0 + kb*32 + (r/4)*8 + hl*4 + r%4
-    const bool masked = (kv0 + BN > seq_len) || (CAUSAL && kv0 + BN - 1 > wq0);
-    const int lim = (CAUSAL ? min(t, seq_len - 1) : seq_len - 1) - (kv0 + hl * 4);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      // P^T and dS^T in place; key of register r: kv0 + kb*32 + (r/4)*8 + hl*4 + r%4
+      const int lim = (CAUSAL ? min(t, seq_len - 1) : seq_len - 1) - (kv0 + kb * 32 + hl * 4);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -lse2));
-        if (masked && kb * 32 + (r >> 2) * 8 + (r & 3) > lim) p = 0.f;
-        s[kb][r] = p * (dp[kb][r] - dlt);
+        float p = fast_exp2(__builtin_fmaf(s[r], a.c, -lse2));
+        if ((r >> 2) * 8 + (r & 3) > lim) p = 0.f;
+        s[r] = p * (dp[r] - dlt);
       }
-    // dQ^T += K^T dS^T, 16 keys at a time
+      // dQ^T += K^T dS^T, 16 keys at a time
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const bf16x8 dsf = pack_chunk(s, kc);
-      const char* kk = kt + kc * 16 * ROWB;
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 w;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x4 lo = ds_read_tr16(kk + voff[0][db]);
-        const bf16x4 hi = ds_read_tr16(kk + voff[1][db]);
-        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                            dsf, dqacc[db], 0, 0, 0);
+        for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(s[8 * c2 + 2 * jj], s[8 * c2 + 2 * jj + 1]);
+        const bf16x8 dsf = __builtin_bit_cast(bf16x8, w);
+        const char* kk = kt + (kb * 2 + c2) * 16 * ROWB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x4 lo = ds_read_tr16(kk + voff[0][db]);
+          const bf16x4 hi = ds_read_tr16(kk + voff[1][db]);
+          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                              dsf, dqacc[db], 0, 0, 0);
+        }
       }
     }
   }
@@ -264,7 +257,8 @@ __global__ void __launch_bounds__(bwd::NW * 64) bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 
 template <int D, bool CAUSAL, bool PACKED>
-__global__ void __launch_bounds__(bwd::NW * 64) bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(bwd::NW * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
+bwd_dkdv_kernel(BwdArgs a) {
   using namespace bwd;
   constexpr int ROWB = D * 2, TILE = BN * ROWB;
   constexpr int CPW = TILE / 1024 / NW;
@@ -374,7 +368,7 @@ __global__ void __launch_bounds__(bwd::NW * 64) bwd_dkdv_kernel(BwdArgs a) {
     // products into dV and dK, so only one half's scores are live at a time
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      __builtin_amdgcn_sched_barrier(0);       // keep each half's loads inside the half
+      __builtin_amdgcn_sched_barrier(0);       // one half's loads at a time: fewer live registers
       f32x16 s, dp;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
