@@ -33,12 +33,20 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
                                scores, one key), key-shift invariance; planted
                                mistakes each trip a pin
   backward.row_dot             pinned: rowsum(dO * O) = rowsum(P * dP)
+  rotation.hadamard            pinned (tests/test_rotation_oracle.py): scipy's
+                               hadamard, the closed form of the entries
+  rotation.rotate              pinned: orthogonality, one-hot rows, inner
+                               products times d, sums beyond float64 (an fp32
+                               tie broken at 2^-80), plain-loop sums of bf16
+                               rows, attention invariance with scale / d
+  rotation.rotate_quantize_blocks  pinned: a rotated one-hot block; planted
+                               mistakes each trip a pin
 """
 from .exact import (attention, attention_rows, online_softmax_states,
                         e4m3_decode, bf16_decode, dequantize_e4m3_blocks,
                         visible_keys)
-from . import backward, quantize
+from . import backward, quantize, rotation
 
 __all__ = ["attention", "attention_rows", "online_softmax_states",
            "e4m3_decode", "bf16_decode", "dequantize_e4m3_blocks", "visible_keys",
-           "backward", "quantize"]
+           "backward", "quantize", "rotation"]
