@@ -19,7 +19,9 @@ page names no particular matrix.  Readings taken here:
     change of scale is exact); the per-block scale of the quantiser absorbs
     the sqrt(d) growth of the magnitudes;
   * the rotated value is the exact product rounded once to fp32 (round to
-    nearest, ties to even), and the block quantiser of oracle.quantize then
+    nearest, ties to even); a sum that is exactly zero is +0 (the exact
+    value carries no sign, and its e4m3 byte is then 0x00); the block
+    quantiser of oracle.quantize then
     works on those fp32 values unchanged: s = amax / 448 in fp32 and each
     byte = e4m3(RN_fp32(x / s)).
 
@@ -95,6 +97,7 @@ def rotate(x, signs) -> np.ndarray:
             fr = [Fraction(float(v)) for v in flat[r]]
             for j in range(d):
                 out[r, j] = _round_fraction_to_f32(sum((f * int(m[i, j]) for i, f in enumerate(fr)), Fraction(0)))
+    out += np.float32(0.0)                          # an exact zero is +0
     return out.reshape(x.shape)
 
 

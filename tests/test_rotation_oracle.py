@@ -123,6 +123,18 @@ def pin_rotated_one_hot_block():
     assert np.all(sc == np.float32(np.float32(3.0) / np.float32(448.0)))
 
 
+def pin_zero_rows_are_positive_zero():
+    # all-zero rows: every rotated value is exactly zero, stored as +0, so
+    # every byte is 0x00 whatever the signs (all negative included)
+    d = 64
+    x = np.zeros((1, 128, 1, d))
+    for s in (np.full(d, -1), _signs(d, 4)):
+        y = rot.rotate(x, s)
+        assert not np.any(np.signbit(y))
+        q, sc = rot.rotate_quantize_blocks(x, s)
+        assert np.all(q == 0) and np.all(sc == 1.0)
+
+
 def pin_outlier_spread():
     # the purpose: one +-20 outlier in a row of N(0,1) values dominates the
     # row's maximum; after the rotation the maximum over the rms is small
