@@ -290,6 +290,58 @@ def extra_quantize(args):
     print(json.dumps(res), flush=True)
 
 
+def extra_rotate(args):
+    """The rotating quantiser (random-sign Hadamard rotation, then e4m3 block
+    quantisation) on q and k of the fp8 workload ([2, 8192, 16, 128] bf16
+    each); HBM roofline as the plain quantiser (2 bytes read and 1 written
+    per element, one fp32 scale per block)."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    import workloads as W
+    w5 = W.workload(5)
+    dev = torch.device("cuda:0")
+    B, N, H, d = w5.B, w5.N, w5.H, w5.d
+    shape = (B, N, H, d)
+    nb = (N + 127) // 128
+
+    def dev16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xs = [dev16(W.normal_bf16(7100 + i, shape, True)) for i in range(2)]
+    ys = [torch.empty(shape, dtype=torch.uint8, device=dev) for _ in range(2)]
+    ss = [torch.empty((B, H, nb), dtype=torch.float32, device=dev) for _ in range(2)]
+    signs = torch.from_numpy(W.random_signs(7102, d)).to(dev)
+
+    def step():
+        for x, y, sc in zip(xs, ys, ss):
+            ia.attn_quantize_fp8_rotated(x, y, sc, signs, B, H, N, d)
+    med, mean = _time_launches(step, args.steps, args.warmup)
+    elems = B * N * H * d
+    per_launch = elems * 3 + B * H * nb * 4
+    gbps = per_launch / (mean / 2 * 1e-3) / 1e9
+
+    res = {"metric": "random-sign Hadamard rotation + bf16 -> e4m3 block quantisation, GB/s of algorithmic HBM "
+                     "traffic", "value": round(gbps, 1), "unit": "GB/s", "higher_is_better": True, "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(mean, 5),
+           "per_step_ms_median": round(med, 5), "dtype": "f64",
+           "data": "synthetic (seeded numpy PCG64 bf16 inputs with 1% +-20 outliers; seeded signs)",
+           "config": {"workload": "rotate and quantise q and k of fp8_block_scaled_causal_b2_h16_n8192_d128 "
+                                  "(one step = 2 launches)",
+                      "kernel": "quantize_fp8_rot_kernel<128,fixed>",
+                      "algorithmic_bytes_per_launch": per_launch},
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK, 4), "traffic": None}}
+    if not args.no_cpu_baseline:
+        import oracle.rotation as orot
+        x_h = W.bf16_bits_to_f32(W.normal_bf16(7100, shape, True))[:, :, :1]
+        t0 = time.perf_counter()
+        orot.rotate_quantize_blocks(x_h, W.random_signs(7102, d))
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(x_h.size * 3 / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"one head of q ({x_h.size} elements), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def extra_fp8_packed(args):
     """fp8 attention over the packed workload's documents: bf16 q, k, v
     quantised by attn_quantize_fp8 with document-local scales, then
@@ -428,7 +480,7 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB (the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--extra", choices=["quantize", "fp8_packed", "bwd"], default=None,
+    ap.add_argument("--extra", choices=["quantize", "rotate", "fp8_packed", "bwd"], default=None,
                     help="instead of the headline line, time the e4m3 block quantiser, "
                          "packed-document fp8 attention or the bf16 backward (on --workload)")
     args = ap.parse_args()
@@ -447,6 +499,9 @@ def main():
         return
     if args.extra == "fp8_packed":
         extra_fp8_packed(args)
+        return
+    if args.extra == "rotate":
+        extra_rotate(args)
         return
     if args.extra == "bwd":
         extra_bwd(args)

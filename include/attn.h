@@ -47,6 +47,7 @@
  *   attn_fwd_fp8: e4m3 q/k/v with per-128-token block scales, o bf16, d = 128,
  *                 fixed length or packed documents.
  *   attn_quantize_fp8: bf16 -> e4m3 with those block scales, d in {64, 128}.
+ *   attn_quantize_fp8_rotated: the same after a random-sign Hadamard rotation.
  *   attn_bwd:     bf16 gradients of attn_fwd (bf16 output), d in {64, 128}.
  *   Anything else returns an error; there is no fallback path.
  *
@@ -202,6 +203,33 @@ ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o
  */
 ATTN_API int attn_quantize_fp8(const void* x, void* y, float* scales, int B, int H, int N, int d,
                                const int32_t* cu_seqlens, void* stream);
+
+/*
+ * attn_quantize_fp8_rotated - incoherent processing before the block
+ * quantisation: the FlashAttention-3 part of "FlashAttention, pelatihan
+ * multi-GPU, dan kuantisasi bobot" (section 1) multiplies Q and K by a random
+ * orthogonal matrix so that outliers are spread before fp8 rounding.  Each
+ * row x (one token, one head, d coordinates) becomes
+ *     z = x diag(signs) H_d,
+ * H_d the Sylvester Hadamard matrix (entry (i, j) = (-1)^popcount(i & j)),
+ * unnormalised: diag(signs) H_d times its transpose is d I, so
+ * (Q M)(K M)^T = d Q K^T and attention on the rotated operands takes
+ * scale / d.  z is the exact signed sum rounded once to fp32 (exact whenever
+ * the nonzero entries of a row span at most 38 binades of exponent; beyond
+ * that the fp64 sum may be rounded before the fp32 rounding).  z then goes
+ * through the block quantisation of attn_quantize_fp8 (amax of |z| per
+ * block, s = amax / 448, e4m3(z / s)).  Rotate Q and K with the same signs;
+ * V is quantised unrotated (attn_quantize_fp8).
+ *   x, y, scales, B, H, N, d, cu_seqlens, stream
+ *               as attn_quantize_fp8 (x finite, |x| < 2^119 so that sums of d
+ *               values stay finite in fp32).
+ *   signs       device int8[d], 16-byte aligned: coordinate i is negated when
+ *               signs[i] < 0 (so +1 / -1 as drawn; any other value counts by
+ *               its sign).  Read only.
+ *   Errors as attn_quantize_fp8, plus ATTN_ERR_NULL / _ALIGN for signs.
+ */
+ATTN_API int attn_quantize_fp8_rotated(const void* x, void* y, float* scales, const int8_t* signs, int B, int H,
+                                       int N, int d, const int32_t* cu_seqlens, void* stream);
 
 /* attn_status_str - static, NUL-terminated description of a status code
  * (unknown codes give "unknown status").  Never NULL; do not free. */

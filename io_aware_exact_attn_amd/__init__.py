@@ -53,6 +53,8 @@ lib.attn_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _vp, _vp]
 lib.attn_bwd.restype = _i
 lib.attn_quantize_fp8.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
 lib.attn_quantize_fp8.restype = _i
+lib.attn_quantize_fp8_rotated.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
+lib.attn_quantize_fp8_rotated.restype = _i
 lib.attn_status_str.argtypes = [_i]
 lib.attn_status_str.restype = ctypes.c_char_p
 lib.attn_kernel_name.argtypes = [_i, _i, _i, _i, _i]
@@ -126,6 +128,17 @@ def attn_quantize_fp8(x, y, scales, B, H, N, d, cu_seqlens=None, stream=None, ch
                                _ptr(cu_seqlens), _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_quantize_fp8")
+    return st
+
+
+def attn_quantize_fp8_rotated(x, y, scales, signs, B, H, N, d, cu_seqlens=None, stream=None,
+                              check: bool = True) -> int:
+    """Enqueue the random-sign Hadamard rotation plus e4m3 block quantisation
+    (see ``attn_quantize_fp8_rotated``); ``signs`` is a device int8 tensor of d."""
+    st = lib.attn_quantize_fp8_rotated(_ptr(x), _ptr(y), _ptr(scales), _ptr(signs), int(B), int(H), int(N),
+                                       int(d), _ptr(cu_seqlens), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_quantize_fp8_rotated")
     return st
 
 

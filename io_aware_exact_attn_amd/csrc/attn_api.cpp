@@ -138,6 +138,24 @@ ATTN_API int attn_quantize_fp8(const void* x, void* y, float* scales, int B, int
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+ATTN_API int attn_quantize_fp8_rotated(const void* x, void* y, float* scales, const int8_t* signs, int B, int H,
+                                       int N, int d, const int32_t* cu_seqlens, void* stream) {
+  if (!x || !y || !scales || !signs) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * N * H >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(scales) || !aligned16(signs)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
+  if (iaea::quantize_fp8_grid(B, H, N, cu_seqlens != nullptr) >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  iaea::QuantArgs a{};
+  a.x = x; a.y = y; a.scales = scales; a.cu_seqlens = cu_seqlens; a.signs = signs;
+  a.B = B; a.H = H; a.N = N;
+  a.nsb = (N + 127) / 128 + (cu_seqlens ? B : 0);
+  const hipError_t e = iaea::launch_quantize_fp8_rotated(a, d, cu_seqlens != nullptr,
+                                                         reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 ATTN_API const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

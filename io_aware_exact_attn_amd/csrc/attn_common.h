@@ -79,6 +79,7 @@ struct QuantArgs {
   void* y;                   // e4m3 output, same layout
   float* scales;             // [B][H][nsb] or packed [H][nsb]
   const int32_t* cu_seqlens; // packed documents, device, B + 1 entries
+  const int8_t* signs;       // rotating quantiser: d random signs (+1 / -1), device
   int B, H, N;
   int nsb;                   // scale slots per (sequence, head): ceil(N / 128), packed + B
 };

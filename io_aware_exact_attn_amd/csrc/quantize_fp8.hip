@@ -152,6 +152,142 @@ __global__ void __launch_bounds__(qz::NT) quantize_fp8_kernel(QuantArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Incoherent processing ("FlashAttention, pelatihan multi-GPU, dan kuantisasi
+// bobot", section 1, its FlashAttention-3 part: Q and K multiplied by a random
+// orthogonal matrix before quantisation, to soften outliers).  The matrix is
+// M = diag(s) H_d, random signs on the input coordinates and then the
+// Sylvester Hadamard matrix (entry (i, j) = (-1)^popcount(i & j)), left
+// unnormalised (M M^T = d I: the attention on rotated Q and K takes scale / d).
+// Each rotated value is a signed sum of d bf16 values; the sum is taken in
+// fp64, exact whenever the row's nonzero exponents span at most 38 binades
+// (a bf16 value is an 8-bit integer times a power of two), and rounded once
+// to fp32 (a sum that is exactly zero as +0); the block quantisation above
+// then runs on those fp32 values.
+//
+// MI355X mapping: one workgroup per 128-token block as above; a token row is
+// spread over D / 16 lanes, 16 coordinates each (two 16-byte loads), and the
+// transform is the in-place fast Walsh-Hadamard butterfly: four stages inside
+// the lane's registers, then log2(D / 16) stages across the row's lanes with
+// xor shuffles.  The block maximum is taken on the fp32 bit patterns.
+// ---------------------------------------------------------------------------
+template <int D, bool PACKED>
+__global__ void __launch_bounds__(qz::NT) quantize_fp8_rot_kernel(QuantArgs a) {
+  constexpr int LPR = D / 16;                 // lanes per token row
+  constexpr int RPP = qz::NT / LPR;           // token rows per pass
+  constexpr int NP = qz::BLK / RPP;           // passes per block
+  const int tid = threadIdx.x;
+  const int li = tid % LPR;                   // this lane's 16 coordinates: li * 16 ...
+  const int64_t rs = (int64_t)a.H * D;
+  QItem it;
+  if (!q_item<PACKED>(a, blockIdx.x, D, it)) return;
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x + it.base;
+  uint8_t* __restrict__ y = (uint8_t*)a.y + it.base;
+
+  u32x4 raw[NP][2];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int row = p * RPP + tid / LPR;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      raw[p][c] = row < it.nt ? *(const u32x4*)(x + row * rs + li * 16 + c * 8) : (u32x4){0u, 0u, 0u, 0u};
+  }
+  // sign flips as xor masks on the bf16 pairs: word w of chunk c holds
+  // coordinates 8c + 2w (low half) and 8c + 2w + 1 (high half)
+  const u32x4 sg = *(const u32x4*)(a.signs + li * 16);
+  uint32_t flip[2][4];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int e0 = 8 * c + 2 * w, e1 = e0 + 1;
+      const uint32_t b0 = (sg[e0 >> 2] >> ((e0 & 3) * 8 + 7)) & 1u;
+      const uint32_t b1 = (sg[e1 >> 2] >> ((e1 & 3) * 8 + 7)) & 1u;
+      flip[c][w] = (b0 << 15) | (b1 << 31);
+    }
+
+  float r[NP][16];
+  uint32_t mb = 0;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    double v[16];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t u = raw[p][c][w] ^ flip[c][w];
+        v[8 * c + 2 * w] = (double)__uint_as_float(u << 16);
+        v[8 * c + 2 * w + 1] = (double)__uint_as_float(u & 0xffff0000u);
+      }
+#pragma unroll
+    for (int hb = 1; hb < 16; hb <<= 1)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!(e & hb)) {
+          const double s0 = v[e], s1 = v[e + hb];
+          v[e] = s0 + s1;
+          v[e + hb] = s0 - s1;
+        }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) {
+      const bool upper = (li & m) != 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const double o = __shfl_xor(v[e], m);
+        v[e] = upper ? o - v[e] : v[e] + o;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      r[p][e] = (float)(v[e] + 0.0);          // + 0.0: an exact zero sum becomes +0
+      mb = max(mb, __float_as_uint(r[p][e]) & 0x7fffffffu);
+    }
+  }
+
+  // block maximum: wave, then workgroup
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off));
+  __shared__ uint32_t wmax[qz::NT / 64];
+  if ((tid & 63) == 0) wmax[tid >> 6] = mb;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < qz::NT / 64; ++w) mb = max(mb, wmax[w]);
+  const float amax = __uint_as_float(mb);
+  const float s = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.f);
+  const float rcp = __fdiv_rn(1.f, s);
+  if (tid == 0) a.scales[it.sidx] = s;
+  auto quot = [&](float xv) __attribute__((always_inline)) {
+    const float q0 = xv * rcp;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, xv), rcp, q0);
+    return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q1, s, xv), rcp, q1), xv);
+  };
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int row = p * RPP + tid / LPR;
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(quot(r[p][4 * w]), quot(r[p][4 * w + 1]), 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(quot(r[p][4 * w + 2]), quot(r[p][4 * w + 3]), word, true);
+      out[w] = (uint32_t)word;
+    }
+    if (row < it.nt) *(u32x4*)(y + row * rs + li * 16) = out;
+  }
+}
+
+template <int D, bool PACKED>
+static hipError_t launch_qr(const QuantArgs& a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.nsb * a.H * (PACKED ? 1 : a.B);
+  void* args[] = {const_cast<QuantArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_fp8_rot_kernel<D, PACKED>), dim3((unsigned)grid),
+                         dim3(qz::NT), args, 0, st);
+}
+
+hipError_t launch_quantize_fp8_rotated(const QuantArgs& a, int d, bool packed, hipStream_t st) {
+  if (d == 128) return packed ? launch_qr<128, true>(a, st) : launch_qr<128, false>(a, st);
+  return packed ? launch_qr<64, true>(a, st) : launch_qr<64, false>(a, st);
+}
+
 template <int D, bool PACKED>
 static hipError_t launch_q(const QuantArgs& a, hipStream_t st) {
   const int64_t grid = (int64_t)a.nsb * a.H * (PACKED ? 1 : a.B);

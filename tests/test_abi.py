@@ -26,7 +26,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_bwd",
+    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_quantize_fp8_rotated", "attn_bwd",
                                          "attn_status_str", "attn_kernel_name"}
 
 
@@ -104,6 +104,24 @@ def quant(**kw):
 ])
 def test_attn_quantize_fp8_rejects(kw, status):
     assert quant(**kw) == status
+
+
+def quant_rot(**kw):
+    args = dict(x=P, y=P, scales=P, signs=P, B=1, H=2, N=300, d=128, cu_seqlens=None, stream=0)
+    args.update(kw)
+    return ia.attn_quantize_fp8_rotated(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ia.ATTN_ERR_NULL), (dict(signs=None), ia.ATTN_ERR_NULL), (dict(scales=None), ia.ATTN_ERR_NULL),
+    (dict(B=0), ia.ATTN_ERR_SHAPE), (dict(N=0), ia.ATTN_ERR_SHAPE),
+    (dict(B=1 << 16, H=1 << 8, N=1 << 8), ia.ATTN_ERR_SHAPE),
+    (dict(d=32), ia.ATTN_ERR_UNSUPPORTED), (dict(d=256), ia.ATTN_ERR_UNSUPPORTED),
+    (dict(signs=MIS), ia.ATTN_ERR_ALIGN), (dict(y=MIS), ia.ATTN_ERR_ALIGN), (dict(cu_seqlens=MIS), ia.ATTN_ERR_ALIGN),
+    (dict(cu_seqlens=P, B=1 << 30, H=4, N=1), ia.ATTN_ERR_SHAPE),
+])
+def test_attn_quantize_fp8_rotated_rejects(kw, status):
+    assert quant_rot(**kw) == status
 
 
 def bwd(**kw):

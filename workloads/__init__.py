@@ -219,6 +219,13 @@ def varlen_lengths(seed: int, total: int = 32768, mean: int = 1024,
     return np.asarray(out, dtype=np.int64)
 
 
+def random_signs(seed: int, d: int) -> np.ndarray:
+    """d independent fair +-1 signs (int8), the random diagonal of a
+    sign-randomised Hadamard rotation."""
+    u = np.random.Generator(np.random.PCG64(seed)).integers(0, 2, size=d)
+    return np.where(u == 1, -1, 1).astype(np.int8)
+
+
 def cu_seqlens_from_lengths(lengths) -> np.ndarray:
     lengths = np.asarray(lengths, dtype=np.int64)
     return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
