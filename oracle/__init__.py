@@ -41,12 +41,19 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
                                rows, attention invariance with scale / d
   rotation.rotate_quantize_blocks  pinned: a rotated one-hot block; planted
                                mistakes each trip a pin
+  mx.quantize_mx_d / _tokens   pinned (tests/test_mx_oracle.py): hand-computed
+                               blocks (power-of-two maximum, floor of the
+                               exponent, saturation, all-zero, small elements),
+                               the format's error bound, block orientation,
+                               document-local restart, causality of scales;
+                               planted mistakes each trip a pin
+  mx.dequantize_mx_*           pinned: exact on e4m3-grid values, error bound
 """
 from .exact import (attention, attention_rows, online_softmax_states,
                         e4m3_decode, bf16_decode, dequantize_e4m3_blocks,
                         visible_keys)
-from . import backward, quantize, rotation
+from . import backward, mx, quantize, rotation
 
 __all__ = ["attention", "attention_rows", "online_softmax_states",
            "e4m3_decode", "bf16_decode", "dequantize_e4m3_blocks", "visible_keys",
-           "backward", "quantize", "rotation"]
+           "backward", "mx", "quantize", "rotation"]
