@@ -48,6 +48,7 @@
  *                 fixed length or packed documents.
  *   attn_quantize_fp8: bf16 -> e4m3 with those block scales, d in {64, 128}.
  *   attn_quantize_fp8_rotated: the same after a random-sign Hadamard rotation.
+ *   attn_quantize_mxfp8: bf16 -> MXFP8 (E8M0 scale per 32 elements), d in {64, 128}.
  *   attn_bwd:     bf16 gradients of attn_fwd (bf16 output), d in {64, 128}.
  *   Anything else returns an error; there is no fallback path.
  *
@@ -230,6 +231,33 @@ ATTN_API int attn_quantize_fp8(const void* x, void* y, float* scales, int B, int
  */
 ATTN_API int attn_quantize_fp8_rotated(const void* x, void* y, float* scales, const int8_t* signs, int B, int H,
                                        int N, int d, const int32_t* cu_seqlens, void* stream);
+
+/*
+ * attn_quantize_mxfp8 - MXFP8 quantisation of a bf16 tensor: e4m3 elements
+ * with one power-of-two scale per block of 32 elements, stored as an E8M0
+ * byte (exponent + 127).  FLAMIA ("FLAMIA: Blackwell Üzerinde Hızlı ve
+ * Nedensel Olarak Güvenli Eğitim İçin Flash Mikro-Ölçeklemeli Dikkat
+ * Mekanizması", section "FLAMIA Mimarisi ve Temel Tasarım İlkeleri") runs
+ * attention on MXFP8 operands.  For a block with maximum magnitude amax:
+ *     e = floor(log2 amax) - 8, clamped to [-127, 127] (e = 0 if all zero),
+ *     byte = e4m3(x / 2^e), nearest with ties to even, clamped to +-448.
+ *   along_tokens = 0 (Q and K): blocks are 32 consecutive coordinates of one
+ *               token and head; scales uint8 [B][N][H][d / 32] (packed
+ *               [N][H][d / 32]); cu_seqlens is accepted and not used (these
+ *               blocks never cross a token).
+ *   along_tokens = 1 (V): blocks are 32 consecutive tokens of one head and
+ *               coordinate; scales uint8 [B][H][ceil(N / 32)][d], block k of
+ *               (b, h) covering tokens 32k .. 32k + 31; packed:
+ *               [H][ceil(N / 32) + B][d], blocks restarting at each document's
+ *               first token, block k of document j in slot cu[j] / 32 + j + k
+ *               (slots no block maps to are left untouched).
+ *   x, y, B, H, N, d, cu_seqlens, stream
+ *               as attn_quantize_fp8 (x finite; y fully overwritten).
+ *   Errors as attn_quantize_fp8, plus ATTN_ERR_UNSUPPORTED for along_tokens
+ *   other than 0 or 1.
+ */
+ATTN_API int attn_quantize_mxfp8(const void* x, void* y, uint8_t* scales, int B, int H, int N, int d,
+                                 const int32_t* cu_seqlens, int along_tokens, void* stream);
 
 /* attn_status_str - static, NUL-terminated description of a status code
  * (unknown codes give "unknown status").  Never NULL; do not free. */

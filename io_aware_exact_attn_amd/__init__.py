@@ -55,6 +55,8 @@ lib.attn_quantize_fp8.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
 lib.attn_quantize_fp8.restype = _i
 lib.attn_quantize_fp8_rotated.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
 lib.attn_quantize_fp8_rotated.restype = _i
+lib.attn_quantize_mxfp8.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _vp]
+lib.attn_quantize_mxfp8.restype = _i
 lib.attn_status_str.argtypes = [_i]
 lib.attn_status_str.restype = ctypes.c_char_p
 lib.attn_kernel_name.argtypes = [_i, _i, _i, _i, _i]
@@ -139,6 +141,17 @@ def attn_quantize_fp8_rotated(x, y, scales, signs, B, H, N, d, cu_seqlens=None, 
                                        int(d), _ptr(cu_seqlens), _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_quantize_fp8_rotated")
+    return st
+
+
+def attn_quantize_mxfp8(x, y, scales, B, H, N, d, cu_seqlens=None, along_tokens=0, stream=None,
+                        check: bool = True) -> int:
+    """Enqueue the bf16 -> MXFP8 quantisation (see ``attn_quantize_mxfp8``):
+    blocks of 32 along d (Q, K) or, with ``along_tokens``, along tokens (V)."""
+    st = lib.attn_quantize_mxfp8(_ptr(x), _ptr(y), _ptr(scales), int(B), int(H), int(N), int(d), _ptr(cu_seqlens),
+                                 int(along_tokens), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_quantize_mxfp8")
     return st
 
 

@@ -156,6 +156,26 @@ ATTN_API int attn_quantize_fp8_rotated(const void* x, void* y, float* scales, co
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+ATTN_API int attn_quantize_mxfp8(const void* x, void* y, uint8_t* scales, int B, int H, int N, int d,
+                                 const int32_t* cu_seqlens, int along_tokens, void* stream) {
+  if (!x || !y || !scales) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * N * H >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (along_tokens != 0 && along_tokens != 1) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(scales)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
+  const bool packed = cu_seqlens != nullptr;
+  iaea::QuantArgs a{};
+  a.x = x; a.y = y; a.scales = reinterpret_cast<float*>(scales); a.cu_seqlens = cu_seqlens;
+  a.B = B; a.H = H; a.N = N;
+  a.nsb = (N + 31) / 32 + (packed ? B : 0);
+  if (along_tokens && ((int64_t)a.nsb * H * (packed ? 1 : B) + 3) / 4 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  const hipError_t e = iaea::launch_quantize_mxfp8(a, d, packed, along_tokens == 1,
+                                                   reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 ATTN_API const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -23,6 +23,7 @@ int bwd_rows_per_workgroup();
 // bf16 -> e4m3 with per-128-token block scales; d in {64, 128}.
 hipError_t launch_quantize_fp8(const QuantArgs& a, int d, bool packed, hipStream_t st);
 hipError_t launch_quantize_fp8_rotated(const QuantArgs& a, int d, bool packed, hipStream_t st);
+hipError_t launch_quantize_mxfp8(const QuantArgs& a, int d, bool packed, bool tokens, hipStream_t st);
 int64_t quantize_fp8_grid(int B, int H, int N, bool packed);
 
 }  // namespace iaea

@@ -26,7 +26,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_quantize_fp8_rotated", "attn_bwd",
+    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_quantize_fp8_rotated", "attn_quantize_mxfp8", "attn_bwd",
                                          "attn_status_str", "attn_kernel_name"}
 
 
@@ -122,6 +122,23 @@ def quant_rot(**kw):
 ])
 def test_attn_quantize_fp8_rotated_rejects(kw, status):
     assert quant_rot(**kw) == status
+
+
+def quant_mx(**kw):
+    args = dict(x=P, y=P, scales=P, B=1, H=2, N=300, d=128, cu_seqlens=None, along_tokens=0, stream=0)
+    args.update(kw)
+    return ia.attn_quantize_mxfp8(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ia.ATTN_ERR_NULL), (dict(scales=None), ia.ATTN_ERR_NULL),
+    (dict(B=0), ia.ATTN_ERR_SHAPE), (dict(N=0), ia.ATTN_ERR_SHAPE),
+    (dict(B=1 << 16, H=1 << 8, N=1 << 8), ia.ATTN_ERR_SHAPE),
+    (dict(d=96), ia.ATTN_ERR_UNSUPPORTED), (dict(along_tokens=2), ia.ATTN_ERR_UNSUPPORTED),
+    (dict(y=MIS), ia.ATTN_ERR_ALIGN), (dict(scales=MIS), ia.ATTN_ERR_ALIGN), (dict(cu_seqlens=MIS), ia.ATTN_ERR_ALIGN),
+])
+def test_attn_quantize_mxfp8_rejects(kw, status):
+    assert quant_mx(**kw) == status
 
 
 def bwd(**kw):
