@@ -49,6 +49,7 @@
  *   attn_quantize_fp8: bf16 -> e4m3 with those block scales, d in {64, 128}.
  *   attn_quantize_fp8_rotated: the same after a random-sign Hadamard rotation.
  *   attn_quantize_mxfp8: bf16 -> MXFP8 (E8M0 scale per 32 elements), d in {64, 128}.
+ *   attn_fwd_mxfp8: MXFP8 q/k/v, o bf16, d = 128, fixed length or packed documents.
  *   attn_bwd:     bf16 gradients of attn_fwd (bf16 output), d in {64, 128}.
  *   Anything else returns an error; there is no fallback path.
  *
@@ -180,6 +181,32 @@ ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const int32_t* cu_seqlens, void* stream);
 
 /*
+ * attn_fwd_mxfp8 - exact attention forward on MXFP8 operands (d = 128), the
+ * micro-scaled FP8 path of FLAMIA ("FLAMIA: Blackwell Üzerinde Hızlı ve
+ * Nedensel Olarak Güvenli Eğitim İçin Flash Mikro-Ölçeklemeli Dikkat
+ * Mekanizması", section "FLAMIA Mimarisi ve Temel Tasarım İlkeleri"), with the
+ * attention itself as attn_fwd.  Operands as attn_quantize_mxfp8 writes them:
+ *   q, k        e4m3 bytes [B][N][H][128] (packed [N][H][128]), with
+ *   q_scale, k_scale   E8M0 bytes [B][N][H][4] (packed [N][H][4]): element d
+ *               of a token and head is e4m3(byte) * 2^(scale[d / 32] - 127).
+ *               Each scale depends on its own token only.
+ *   v           e4m3 bytes, same layout, with
+ *   v_scale     E8M0 bytes [B][H][ceil(N / 32)][128] (packed [H][ceil(N / 32)
+ *               + B][128], document-local blocks as attn_quantize_mxfp8):
+ *               token t, coordinate d is e4m3(byte) * 2^(v_scale[t / 32][d] -
+ *               127).  A V scale can depend on later tokens of its own
+ *               32-token block, never on another block.
+ *   Scale bytes must not be 0xFF (the format's NaN); slots no block maps to
+ *   are never read.  o, lse, B, H, N, scale, causal, cu_seqlens, stream as
+ *   attn_fwd_fp8.  P enters P.V as two e4m3 terms with a power of two per
+ *   query and 32-key block.
+ *   Errors as attn_fwd_fp8.
+ */
+ATTN_API int attn_fwd_mxfp8(const void* q, const void* k, const void* v, const uint8_t* q_scale,
+                            const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse, int B, int H,
+                            int N, int d, float scale, int causal, const int32_t* cu_seqlens, void* stream);
+
+/*
  * attn_quantize_fp8 - block-scaled e4m3 quantisation of a bf16 tensor, the
  * step upstream of attn_fwd_fp8: the per-tile scales of the FlashAttention-3
  * part of "FlashAttention, pelatihan multi-GPU, dan kuantisasi bobot"
@@ -265,7 +292,8 @@ ATTN_API const char* attn_status_str(int status);
 
 /* attn_kernel_name - static name of the kernel attn_fwd / attn_fwd_fp8 would
  * launch for these arguments ("" when the arguments are not supported), so a
- * caller can confirm which code path runs.  fp8 != 0 selects attn_fwd_fp8. */
+ * caller can confirm which code path runs.  fp8 = 1 selects attn_fwd_fp8,
+ * fp8 = 2 attn_fwd_mxfp8. */
 ATTN_API const char* attn_kernel_name(int d, int causal, int packed, int dtype, int fp8);
 
 #ifdef __cplusplus

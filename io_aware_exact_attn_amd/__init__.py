@@ -57,6 +57,8 @@ lib.attn_quantize_fp8_rotated.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _v
 lib.attn_quantize_fp8_rotated.restype = _i
 lib.attn_quantize_mxfp8.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _vp]
 lib.attn_quantize_mxfp8.restype = _i
+lib.attn_fwd_mxfp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]
+lib.attn_fwd_mxfp8.restype = _i
 lib.attn_status_str.argtypes = [_i]
 lib.attn_status_str.restype = ctypes.c_char_p
 lib.attn_kernel_name.argtypes = [_i, _i, _i, _i, _i]
@@ -121,6 +123,17 @@ def attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale, 
                           int(causal), _ptr(cu_seqlens), _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_fwd_fp8")
+    return st
+
+
+def attn_fwd_mxfp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale, causal,
+                   cu_seqlens=None, stream=None, check: bool = True) -> int:
+    """Enqueue the MXFP8 attention forward (see ``attn_fwd_mxfp8``)."""
+    st = lib.attn_fwd_mxfp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                            _ptr(o), _ptr(lse), int(B), int(H), int(N), int(d), float(scale),
+                            int(causal), _ptr(cu_seqlens), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_mxfp8")
     return st
 
 

@@ -92,6 +92,31 @@ ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+ATTN_API int attn_fwd_mxfp8(const void* q, const void* k, const void* v, const uint8_t* q_scale,
+                            const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse, int B, int H,
+                            int N, int d, float scale, int causal, const int32_t* cu_seqlens, void* stream) {
+  iaea::FwdArgs a;
+  const int st = check_common(q, k, v, o, lse, B, H, N, scale, causal, a);
+  if (st != ATTN_OK) return st;
+  if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_NULL;
+  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)H * d > ((int64_t)1 << 24)) return ATTN_ERR_SHAPE;
+  if (!aligned16(q_scale) || !aligned16(k_scale) || !aligned16(v_scale)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens && (int64_t)H * ((N + 127) / 128 + B) + 8 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  // V scale rows: ceil(N / 32) blocks per (sequence, head), packed + B
+  if ((int64_t)H * B * ((N + 31) / 32 + 1) * d >= ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;
+  a.q_scale = reinterpret_cast<const float*>(q_scale);
+  a.k_scale = reinterpret_cast<const float*>(k_scale);
+  a.v_scale = reinterpret_cast<const float*>(v_scale);
+  a.cu_seqlens = cu_seqlens;
+  a.nsb = (N + 31) / 32 + (cu_seqlens ? B : 0);
+  a.qsign = std::signbit(scale) ? 0x80808080u : 0u;
+  const hipError_t e = iaea::launch_attn_fwd_mxfp8(a, causal == 1, cu_seqlens != nullptr,
+                                                   reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, float* delta, void* dq, void* dk, void* dv,
                       int B, int H, int N, int d, float scale, int causal,
@@ -191,6 +216,12 @@ ATTN_API const char* attn_status_str(int status) {
 
 ATTN_API const char* attn_kernel_name(int d, int causal, int packed, int dtype, int fp8) {
   if (causal != 0 && causal != 1) return "";
+  if (fp8 == 2) {
+    if (d != 128) return "";
+    static const char* mx[2][2] = {{"attn_fwd_fp8_kernel<full,fixed,mx>", "attn_fwd_fp8_kernel<full,packed,mx>"},
+                                   {"attn_fwd_fp8_kernel<causal,fixed,mx>", "attn_fwd_fp8_kernel<causal,packed,mx>"}};
+    return mx[causal][packed ? 1 : 0];
+  }
   if (fp8) {
     if (d != 128) return "";
     static const char* f8[2][2] = {{"attn_fwd_fp8_kernel<full,fixed>", "attn_fwd_fp8_kernel<full,packed>"},

@@ -27,8 +27,9 @@
 // tile).  P enters P.V as two e4m3 terms with a power-of-two scale per query
 // (both lanes that hold its two 32-key halves use it): with the query's 64
 // weights in the tile summing to less than 2^E, hi = e4m3(P 2^(8-E)) and
-// lo = e4m3((P - hi 2^(E-8)) 2^(12-E)), and the MFMA's per-column E8M0 operand
-// scales apply 2^(E-8) and 2^(E-12) back.  The
+// lo = e4m3((P - hi 2^(E-8)) 2^(13-E)), and the MFMA's E8M0 operand scales
+// apply 2^(E-8) and 2^(E-13) back.  P 2^(8-E) < 256, where e4m3 steps by at
+// most 16, so the remainder is at most 2^(E-5) and lo at most 256 (< 448).  The
 // tile's V scale joins them: its power-of-two part in the same E8M0 scale,
 // the rest f = sv / 2^e in [1, 2) in the exponent of the weights (P' = P f).
 // The accumulator therefore stays in real units, with no per-tile rescale,
@@ -72,16 +73,30 @@ __device__ __forceinline__ i32x2 ds_read_tr8(const char* p) {
 __device__ __forceinline__ f32x16 mfma(const i32x8& a, const i32x8& b, const f32x16& c, uint32_t sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, sb);
 }
+// both operand scales, byte OA of sa and byte OB of sb.  Scale block 0 of the
+// 64-long contraction is bytes 0..15 of every lane's operand and takes its
+// scale from the lane in the lower half-wave; block 1 is bytes 16..31, scaled
+// from the upper half-wave's lane.
+template <int OA, int OB>
+__device__ __forceinline__ f32x16 mfma2(const i32x8& a, const i32x8& b, const f32x16& c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+}
 
 }  // namespace fp8
 
 template <int P> struct F8Parity { static constexpr int value = P; };
 
-template <bool CAUSAL, bool PACKED>
+// MX: MXFP8 operands instead (E8M0 byte scales per 32 elements: along d for
+// Q and K, per token; along 32-token blocks for V, per coordinate), applied by
+// the matrix instruction itself; P's power of two then goes per 32-key block.
+template <bool CAUSAL, bool PACKED, bool MX>
 __global__ void __launch_bounds__(fp8::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 attn_fwd_fp8_kernel(FwdArgs a) {
   using namespace fp8;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
+  // K0 K1 V0 V1, then (MX) the K and V scale bytes of both buffers
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + (MX ? 4 * 256 : 0)];
+  [[maybe_unused]] char* const kscl = smem + 4 * TILE;         // [2][64 keys][4 groups]
+  [[maybe_unused]] char* const vscl = smem + 4 * TILE + 512;   // [2][2 blocks][128 coordinates]
 
   int h, b, seq_start, seq_len, qblk;
   if (!decode_work<BM, CAUSAL, PACKED>(a, blockIdx.x, h, b,
@@ -109,19 +124,36 @@ attn_fwd_fp8_kernel(FwdArgs a) {
   const int64_t sbase = PACKED ? (int64_t)h * a.nsb + seq_start / 128 + b : (int64_t)(b * a.H + h) * a.nsb;
   const float* __restrict__ ks = a.k_scale + sbase;
   const float* __restrict__ vs = a.v_scale + sbase;
-  const float sq = (wq0 < seq_len) ? a.q_scale[sbase + wq0 / 128] : 1.f;
+  const float sq = (!MX && wq0 < seq_len) ? a.q_scale[sbase + wq0 / 128] : 1.f;
   const float cq = a.c * sq;
+  // MX: this lane's query scales (byte 2dc + hl is the group of its operand
+  // block for chunk dc; the upper half-wave shifts it into byte 2dc) and the
+  // base of this (sequence, head)'s rows of V scale blocks
+  [[maybe_unused]] uint32_t qsc = kScaleOne;
+  [[maybe_unused]] const uint8_t* const ksb = (const uint8_t*)a.k_scale + (int64_t)h * 4;
+  [[maybe_unused]] const uint8_t* const vsb =
+      (const uint8_t*)a.v_scale +
+      (PACKED ? (int64_t)h * a.nsb + seq_start / 32 + b : (int64_t)(b * a.H + h) * a.nsb) * D;
+  if constexpr (MX) {
+    const int t = wq0 + l32;
+    if (t < seq_len) {
+      const uint32_t u = *(const uint32_t*)((const uint8_t*)a.q_scale + ((int64_t)(seq_start + t) * a.H + h) * 4);
+      qsc = hl ? (u >> 8) : u;
+    }
+  }
 
-  // ---- Q fragments: 32 bytes (d = dc*64 + 32*half + 0..31) of this lane's query
+  // ---- Q fragments: 32 bytes of this lane's query per 64-coordinate chunk dc:
+  // d = dc*64 + 32*half + 0..31, or for MX (each 16-byte half in its own
+  // 32-coordinate scale block) d = dc*64 + 16*half + 0..15 and + 32
   i32x8 qf[2];
   {
     const int t = wq0 + l32;
     const bool ok = t < seq_len;
-    const uint8_t* p = qg + (int64_t)(seq_start + (ok ? t : 0)) * rs + head_off + 32 * hl;
+    const uint8_t* p = qg + (int64_t)(seq_start + (ok ? t : 0)) * rs + head_off + (MX ? 16 : 32) * hl;
 #pragma unroll
     for (int dc = 0; dc < 2; ++dc) {
       const u32x4 lo = ok ? *(const u32x4*)(p + dc * 64) : (u32x4){0u, 0u, 0u, 0u};
-      const u32x4 hi = ok ? *(const u32x4*)(p + dc * 64 + 16) : (u32x4){0u, 0u, 0u, 0u};
+      const u32x4 hi = ok ? *(const u32x4*)(p + dc * 64 + (MX ? 32 : 16)) : (u32x4){0u, 0u, 0u, 0u};
       qf[dc] = (i32x8){(int)(lo[0] ^ a.qsign), (int)(lo[1] ^ a.qsign), (int)(lo[2] ^ a.qsign), (int)(lo[3] ^ a.qsign),
                        (int)(hi[0] ^ a.qsign), (int)(hi[1] ^ a.qsign), (int)(hi[2] ^ a.qsign), (int)(hi[3] ^ a.qsign)};
     }
@@ -152,6 +184,28 @@ attn_fwd_fp8_kernel(FwdArgs a) {
                                                16, lane_off[cc], 0, 0, 0);
 #endif
   };
+  // MX: the tile's scale bytes, one dword per lane (rows past the end read 0,
+  // a finite scale on zero data): wave 0 the 64 keys' four groups, wave 1 the
+  // two 32-token V blocks' 128 coordinates
+  auto issue_scales = [&](int buf, int j) __attribute__((always_inline)) {
+#if __HIP_DEVICE_COMPILE__
+    if constexpr (MX) {
+      const int kv0 = j * BN;
+      if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(ksb + (int64_t)(seq_start + kv0) * a.H * 4), (short)0,
+            (int)((uint32_t)min(seq_len - kv0, BN) * (uint32_t)a.H * 4u), kBufferFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (IAEA_LDS void*)(kscl + buf * 256), 4, lane * a.H * 4, 0, 0, 0);
+      } else if (wave == 1) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vsb + (int64_t)(kv0 / 32) * D), (short)0, min((seq_len - kv0 + 31) / 32, 2) * D, kBufferFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (IAEA_LDS void*)(vscl + buf * 256), 4, lane * 4, 0, 0, 0);
+      }
+    }
+#else
+    (void)buf; (void)j;
+#endif
+  };
 
   // ---- loop-invariant LDS read offsets.  K fragment: row kb*32 + l32, bytes
   // dc*64 + 32*half + 0..31 (granules 4dc + 2half, +1).  V^T fragment
@@ -163,7 +217,7 @@ attn_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
   for (int dc = 0; dc < 2; ++dc)
 #pragma unroll
-    for (int x = 0; x < 2; ++x) koff[dc][x] = lds_off(l32, 4 * dc + 2 * hl + x);
+    for (int x = 0; x < 2; ++x) koff[dc][x] = lds_off(l32, MX ? 4 * dc + 2 * x + hl : 4 * dc + 2 * hl + x);
   uint32_t voff[4][4];
   {
     const int g16 = lane >> 4;
@@ -190,32 +244,48 @@ attn_fwd_fp8_kernel(FwdArgs a) {
     if (it + 1 < n_iter) {
       issue_tile(kg, P ^ 1, it + 1);
       issue_tile(vg, 2 + (P ^ 1), it + 1);
+      issue_scales(P ^ 1, it + 1);
     }
     if (it < wave_iters) {
       const int kv0 = it * BN;
       const char* kt = smem + P * TILE;
       const char* vt = smem + (2 + P) * TILE;
-      const float sk = ks[kv0 / 128];
-      const float sv = vs[kv0 / 128];
+      const float sk = MX ? 1.f : ks[kv0 / 128];
+      const float sv = MX ? 1.f : vs[kv0 / 128];
       const float ct = cq * sk;
       // sv = f 2^esv with f in [1, 2)
-      const float f = 2.f * __builtin_amdgcn_frexp_mantf(sv);
-      const int esv = __builtin_amdgcn_frexp_expf(sv) - 1;
-      const float lf = __log2f(f);
+      const float f = MX ? 1.f : 2.f * __builtin_amdgcn_frexp_mantf(sv);
+      const int esv = MX ? 0 : __builtin_amdgcn_frexp_expf(sv) - 1;
+      const float lf = MX ? 0.f : __log2f(f);
+      // MX: the scale bytes of this lane's key rows (K) and of its V block
+      [[maybe_unused]] uint32_t ksc[2] = {kScaleOne, kScaleOne};
+      [[maybe_unused]] uint32_t vsc = kScaleOne;
+      if constexpr (MX) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t u = *(const uint32_t*)(kscl + P * 256 + (kb * 32 + l32) * 4);
+          ksc[kb] = hl ? (u >> 8) : u;
+        }
+        const uint8_t* vp = (const uint8_t*)vscl + P * 256 + hl * 128 + l32;
+        vsc = (uint32_t)vp[0] | ((uint32_t)vp[32] << 8) | ((uint32_t)vp[64] << 16) | ((uint32_t)vp[96] << 24);
+      }
 
       // S^T for the two 32-key halves of the tile, masked
       f32x16 s[2];
       auto scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int dc = 0; dc < 2; ++dc) {
+          static_for<2>([&](auto dci) __attribute__((always_inline)) {
+            constexpr int dc = decltype(dci)::value;
             const u32x4 x0 = *(const u32x4*)(kt + kb * 32 * ROWB + koff[dc][0]);
             const u32x4 x1 = *(const u32x4*)(kt + kb * 32 * ROWB + koff[dc][1]);
             const i32x8 kf = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                               (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-            s[kb] = mfma(kf, qf[dc], dc == 0 ? (f32x16){} : s[kb], kScaleOne);
-          }
+            if constexpr (MX)
+              s[kb] = mfma2<2 * dc, 2 * dc>(kf, qf[dc], dc == 0 ? (f32x16){} : s[kb], ksc[kb], qsc);
+            else
+              s[kb] = mfma(kf, qf[dc], dc == 0 ? (f32x16){} : s[kb], kScaleOne);
+          });
         }
         if ((kv0 + BN > seq_len) || (CAUSAL && kv0 + BN - 1 > wq0)) {
           const int lim = (CAUSAL ? min(wq0 + l32, seq_len - 1) : seq_len - 1) - (kv0 + hl * 4);
@@ -227,12 +297,13 @@ attn_fwd_fp8_kernel(FwdArgs a) {
         }
       };
       // P' = exp2(s ct - m + log2 f) = P f in place of the scores; returns the
-      // lane's sum of P'
+      // lane's sum of P' (and, in xb, its sum over each 32-key half)
+      float xb[2];
       auto weights = [&]() __attribute__((always_inline)) -> float {
         const float shift = m_run - lf;
-        float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          float x0 = 0.f, x1 = 0.f;
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
             s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], ct, -shift));
@@ -240,7 +311,9 @@ attn_fwd_fp8_kernel(FwdArgs a) {
             if (r & 2) x1 += s[kb][r] + s[kb][r + 1];
             else       x0 += s[kb][r] + s[kb][r + 1];
           }
-        return x0 + x1;
+          xb[kb] = x0 + x1;
+        }
+        return xb[0] + xb[1];
       };
       scores();
       float lx = weights();
@@ -266,19 +339,32 @@ attn_fwd_fp8_kernel(FwdArgs a) {
 
       // P' as two e4m3 terms with the query's power-of-two scale 2^E above the
       // sum of its 64 weights in this tile: hi = e4m3(P' 2^(8-E)),
-      // lo = e4m3((P' - hi 2^(E-8)) 2^(12-E)).  The conversions apply the
+      // lo = e4m3((P' - hi 2^(E-8)) 2^(13-E)).  The conversions apply the
       // power-of-two part of their scale operand.  The matrix instruction takes
       // one B scale per column, so both lanes holding a query's 32-key halves
       // (l and l ^ 32) must quantise against the same E.
-      const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lx), __float_as_uint(lx), false, false);
-      const float lq = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-      const int E = lq > 0.f ? __builtin_amdgcn_frexp_expf(lq) : 0;
-      const float sh = __builtin_amdgcn_ldexpf(1.f, E - 8), sl = __builtin_amdgcn_ldexpf(1.f, E - 12);
+      // (MX: the instruction scales each 32-key block from its own lane, so E
+      // is per block: block kb's 32 keys are 16 in each of lanes l and l ^ 32.)
+      int Eb[2];
+      if constexpr (MX) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const auto bsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(xb[kb]), __float_as_uint(xb[kb]), false, false);
+          const float bq = __uint_as_float(bsw[0]) + __uint_as_float(bsw[1]);
+          Eb[kb] = bq > 0.f ? __builtin_amdgcn_frexp_expf(bq) : 0;
+        }
+      } else {
+        const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lx), __float_as_uint(lx), false, false);
+        const float lq = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+        Eb[0] = Eb[1] = lq > 0.f ? __builtin_amdgcn_frexp_expf(lq) : 0;
+      }
+      const int E = hl ? Eb[1] : Eb[0];         // the block this lane's operand scale covers
       i32x8 phi, plo;
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         // p index j -> S register j / 16, j % 16: bytes 0..3 of word w are p[4w .. 4w + 3]
         const int j = 4 * w, kb = j >> 4, r = j & 15;
+        const float sh = __builtin_amdgcn_ldexpf(1.f, Eb[kb] - 8), sl = __builtin_amdgcn_ldexpf(1.f, Eb[kb] - 13);
         s16x2 h2 = {0, 0}, l2 = {0, 0};
         h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, s[kb][r], s[kb][r + 1], sh, false);
         h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, s[kb][r + 2], s[kb][r + 3], sh, true);
@@ -290,16 +376,16 @@ attn_fwd_fp8_kernel(FwdArgs a) {
         phi[w] = (int)hw;
         plo[w] = (int)__builtin_bit_cast(uint32_t, l2);
       }
-      // E8M0 scales of the P^T operand: 2^(E-8) and 2^(E-12) times the
+      // E8M0 scales of the P^T operand: 2^(E-8) and 2^(E-13) times the
       // power-of-two part 2^esv of the V scale (clamped to the format's range;
       // a clamp only touches tiles whose weights are ~2^-100 of the row's)
       // (the byte is repeated in all four operand bytes, as the fixed scales are)
       const uint32_t ehi = (uint32_t)min(max(127 + E - 8 + esv, 0), 254) * 0x01010101u;
-      const uint32_t elo = (uint32_t)min(max(127 + E - 12 + esv, 0), 254) * 0x01010101u;
+      const uint32_t elo = (uint32_t)min(max(127 + E - 13 + esv, 0), 254) * 0x01010101u;
 
       // O^T += V^T P'^T (hi and lo terms), 64 keys per MFMA
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      static_for<4>([&](auto dbi) __attribute__((always_inline)) {
+        constexpr int db = decltype(dbi)::value;
         i32x8 vf;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -307,9 +393,14 @@ attn_fwd_fp8_kernel(FwdArgs a) {
           vf[2 * t] = x[0];
           vf[2 * t + 1] = x[1];
         }
-        oacc[db] = mfma(vf, phi, oacc[db], ehi);
-        oacc[db] = mfma(vf, plo, oacc[db], elo);
-      }
+        if constexpr (MX) {
+          oacc[db] = mfma2<db, 0>(vf, phi, oacc[db], vsc, ehi);
+          oacc[db] = mfma2<db, 0>(vf, plo, oacc[db], vsc, elo);
+        } else {
+          oacc[db] = mfma(vf, phi, oacc[db], ehi);
+          oacc[db] = mfma(vf, plo, oacc[db], elo);
+        }
+      });
     }
     __syncthreads();
   };
@@ -317,6 +408,7 @@ attn_fwd_fp8_kernel(FwdArgs a) {
   if (n_iter > 0) {
     issue_tile(kg, 0, 0);
     issue_tile(vg, 2, 0);
+    issue_scales(0, 0);
   }
   __syncthreads();
   for (int it = 0; it < n_iter; it += 2) {
@@ -347,7 +439,7 @@ attn_fwd_fp8_kernel(FwdArgs a) {
   }
 }
 
-template <bool CAUSAL, bool PACKED>
+template <bool CAUSAL, bool PACKED, bool MX>
 static hipError_t launch_fp8(FwdArgs a, hipStream_t st) {
   if (PACKED) {
     a.slots = (a.N + fp8::BM - 1) / fp8::BM + a.B;
@@ -359,13 +451,18 @@ static hipError_t launch_fp8(FwdArgs a, hipStream_t st) {
   const int grid = (a.n_work + kXcds - 1) / kXcds * kXcds;
   a.per_xcd = grid / kXcds;
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<CAUSAL, PACKED>), dim3(grid),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<CAUSAL, PACKED, MX>), dim3(grid),
                          dim3(fp8::NW * 64), args, 0, st);
 }
 
 hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool causal, bool packed, hipStream_t st) {
-  if (packed) return causal ? launch_fp8<true, true>(a, st) : launch_fp8<false, true>(a, st);
-  return causal ? launch_fp8<true, false>(a, st) : launch_fp8<false, false>(a, st);
+  if (packed) return causal ? launch_fp8<true, true, false>(a, st) : launch_fp8<false, true, false>(a, st);
+  return causal ? launch_fp8<true, false, false>(a, st) : launch_fp8<false, false, false>(a, st);
+}
+
+hipError_t launch_attn_fwd_mxfp8(const FwdArgs& a, bool causal, bool packed, hipStream_t st) {
+  if (packed) return causal ? launch_fp8<true, true, true>(a, st) : launch_fp8<false, true, true>(a, st);
+  return causal ? launch_fp8<true, false, true>(a, st) : launch_fp8<false, false, true>(a, st);
 }
 
 }  // namespace iaea

@@ -14,6 +14,7 @@ int bf16_rows_per_workgroup(int d);
 // e4m3 q/k/v with per-128-token scales; d = 128; o bf16; fixed length or
 // packed documents (document-local scale blocks).
 hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool causal, bool packed, hipStream_t st);
+hipError_t launch_attn_fwd_mxfp8(const FwdArgs& a, bool causal, bool packed, hipStream_t st);
 
 // bf16 backward: D = rowsum(dO * O) into a.delta, then dQ, then dK and dV;
 // d in {64, 128}.  Arguments already validated.

@@ -26,7 +26,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_quantize_fp8_rotated", "attn_quantize_mxfp8", "attn_bwd",
+    assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_quantize_fp8_rotated", "attn_quantize_mxfp8", "attn_fwd_mxfp8", "attn_bwd",
                                          "attn_status_str", "attn_kernel_name"}
 
 
