@@ -342,6 +342,79 @@ def extra_rotate(args):
     print(json.dumps(res), flush=True)
 
 
+def extra_mxfp8(args):
+    """MXFP8 attention (attn_fwd_mxfp8) on the fp8 workload's shape and
+    causal mask ([2, 8192, 16, 128]): its bf16 q, k, v (1% +-20 outliers)
+    quantised on the GPU by attn_quantize_mxfp8 (q, k along d; v along
+    tokens); only the attention launch is timed for the headline, the two
+    quantiser orientations are timed beside it."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    import workloads as W
+    w = W.workload(5)
+    dev = torch.device("cuda:0")
+    B, N, H, d = w.B, w.N, w.H, w.d
+    shape = (B, N, H, d)
+
+    def dev16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    bits = [W.normal_bf16(W.tensor_seed(5, t), shape, True) for t in ("q", "k", "v")]
+    xs = [dev16(b) for b in bits]
+    ys = [torch.empty(shape, dtype=torch.uint8, device=dev) for _ in range(3)]
+    ss = [torch.empty((B, N, H, d // 32), dtype=torch.uint8, device=dev) for _ in range(2)]
+    ss.append(torch.empty((B, H, (N + 31) // 32, d), dtype=torch.uint8, device=dev))
+
+    def quant_d():
+        for i in range(2):
+            ia.attn_quantize_mxfp8(xs[i], ys[i], ss[i], B, H, N, d, None, 0)
+
+    def quant_t():
+        ia.attn_quantize_mxfp8(xs[2], ys[2], ss[2], B, H, N, d, None, 1)
+    qd_med, qd_mean = _time_launches(quant_d, args.steps, args.warmup)
+    qt_med, qt_mean = _time_launches(quant_t, args.steps, args.warmup)
+    o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def step():
+        ia.attn_fwd_mxfp8(ys[0], ys[1], ys[2], ss[0], ss[1], ss[2], o, lse, B, H, N, d, w.scale, 1)
+    med, mean = _time_launches(step, args.steps, args.warmup)
+    F = flops(w)
+    tf = F / (mean * 1e-3) / 1e12
+    elems = B * N * H * d
+    qbytes = elems * 3 + elems // 32
+    res = {"metric": "MXFP8 attention fwd TFLOP/s (bf16 causal count, B·H·N²·d)", "value": round(tf, 2),
+           "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(mean, 5), "per_launch_ms_median": round(med, 5), "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp8",
+           "data": "synthetic (the fp8 workload's seeded bf16 q, k, v, quantised to MXFP8 on the GPU)",
+           "config": {"workload": "fp8_block_scaled_causal_b2_h16_n8192_d128 in MXFP8 (E8M0 per 32)", "B": B,
+                      "H": H, "N": N, "d": d, "causal": True, "flop_per_step": F,
+                      "kernel": ia.attn_kernel_name(d, 1, 0, 0, fp8=2),
+                      "quantise_qk_along_d_ms": round(qd_mean, 5),
+                      "quantise_qk_along_d_gbps": round(2 * qbytes / (qd_mean * 1e-3) / 1e9, 1),
+                      "quantise_v_along_tokens_ms": round(qt_mean, 5),
+                      "quantise_v_along_tokens_gbps": round(qbytes / (qt_mean * 1e-3) / 1e9, 1)},
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK["fp8"], "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK["fp8"], 4), "traffic": None}}
+    if not args.no_cpu_baseline:
+        import oracle
+        import oracle.mx as omx
+        h = [(y[:1, :, :1].cpu().numpy(), s_) for y, s_ in zip(ys, (ss[0][:1, :, :1].cpu().numpy(),
+                                                                    ss[1][:1, :, :1].cpu().numpy(),
+                                                                    ss[2][:1, :1].cpu().numpy()))]
+        qd = omx.dequantize_mx_d(*h[0])
+        kd = omx.dequantize_mx_d(*h[1])
+        vd = omx.dequantize_mx_tokens(*h[2])
+        t0 = time.perf_counter()
+        oracle.attention(qd, kd, vd, w.scale, causal=True)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": F / (B * H) / dt / 1e12, "unit": "TFLOP/s", "cores": os.cpu_count(),
+                               "kind": "oracle", "sample": f"one (sequence, head), every row, fp64 oracle on the "
+                                                            f"dequantised MXFP8 operands; {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def extra_fp8_packed(args):
     """fp8 attention over the packed workload's documents: bf16 q, k, v
     quantised by attn_quantize_fp8 with document-local scales, then
@@ -480,7 +553,7 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB (the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--extra", choices=["quantize", "rotate", "fp8_packed", "bwd"], default=None,
+    ap.add_argument("--extra", choices=["quantize", "rotate", "fp8_packed", "mxfp8", "bwd"], default=None,
                     help="instead of the headline line, time the e4m3 block quantiser, "
                          "packed-document fp8 attention or the bf16 backward (on --workload)")
     args = ap.parse_args()
@@ -502,6 +575,9 @@ def main():
         return
     if args.extra == "rotate":
         extra_rotate(args)
+        return
+    if args.extra == "mxfp8":
+        extra_mxfp8(args)
         return
     if args.extra == "bwd":
         extra_bwd(args)
