@@ -80,3 +80,47 @@ def row_dot(o, do) -> np.ndarray:
     o, do = np.asarray(o, dtype=np.float64), np.asarray(do, dtype=np.float64)
     d = (o * do).sum(axis=-1)
     return d.transpose(0, 2, 1) if d.ndim == 3 else d.T
+
+
+def grads_at(q, k, v, do, scale: float, causal: bool, q_rows, k_rows, chunk: int = 1024):
+    """The same gradients for selected rows of one (sequence, head), without
+    an n x n matrix: q, k [n, d], v, do [n, dv] (float64-exact values).
+
+    L_i = logsumexp_j S_ij and D_i = rowsum(dO_i * O_i) are formed for every
+    row, ``chunk`` rows at a time; then dQ at q_rows from P_i. and dP_i., and
+    dK, dV at k_rows from the columns P_.j (every query that sees key j).
+    Returns (dq [len(q_rows), d], dk [len(k_rows), d], dv [len(k_rows), dv],
+    parts), parts holding L, D and O for every row (for error bounds)."""
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    n = q.shape[0]
+    L = np.empty(n)
+    O = np.empty((n, v.shape[1]))
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        s = float(scale) * (q[a:b] @ k.T)
+        if causal:
+            s = np.where(np.arange(n)[None, :] > np.arange(a, b)[:, None], -np.inf, s)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        l = p.sum(axis=1, keepdims=True)
+        L[a:b] = (m + np.log(l))[:, 0]
+        O[a:b] = (p / l) @ v
+    D = (O * do).sum(axis=1)
+    qr = np.asarray(q_rows, dtype=np.int64)
+    kr = np.asarray(k_rows, dtype=np.int64)
+    # dQ rows
+    s = float(scale) * (q[qr] @ k.T)
+    if causal:
+        s = np.where(np.arange(n)[None, :] > qr[:, None], -np.inf, s)
+    p = np.exp(s - L[qr][:, None])
+    dp = do[qr] @ v.T
+    dq = float(scale) * ((p * (dp - D[qr][:, None])) @ k)
+    # dK, dV columns: every query row i against key j
+    s = float(scale) * (q @ k[kr].T)                      # [n, len(k_rows)]
+    if causal:
+        s = np.where(kr[None, :] > np.arange(n)[:, None], -np.inf, s)
+    p = np.exp(s - L[:, None])
+    dp = do @ v[kr].T
+    dk = float(scale) * ((p * (dp - D[:, None])).T @ q)
+    dv = p.T @ do
+    return dq, dk, dv, {"L": L, "D": D, "O": O}

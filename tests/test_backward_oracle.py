@@ -115,6 +115,26 @@ def pin_key_shift_invariance():
         assert np.allclose(dk.sum(axis=1), 0, atol=1e-12)
 
 
+def pin_sampled_rows_torch_autograd():
+    # grads_at against torch autograd (float64) at chosen rows, with a chunk
+    # smaller than the sequence so that the row-chunked pass is exercised
+    import torch
+    n, d = 37, 8
+    q, k, v, do = _rand((n, d)), _rand((n, d)), _rand((n, 5)), _rand((n, 5))
+    rows = [0, 1, 17, 36]
+    for causal in (False, True):
+        tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+        s = 0.3 * tq @ tk.T
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+        (torch.softmax(s, dim=-1) @ tv * torch.tensor(do)).sum().backward()
+        dq, dk, dv, parts = ob.grads_at(q, k, v, do, 0.3, causal, rows, rows, chunk=8)
+        assert np.allclose(dq, tq.grad.numpy()[rows], rtol=1e-11, atol=1e-12)
+        assert np.allclose(dk, tk.grad.numpy()[rows], rtol=1e-11, atol=1e-12)
+        assert np.allclose(dv, tv.grad.numpy()[rows], rtol=1e-11, atol=1e-12)
+        assert np.allclose(parts["L"], torch.logsumexp(s, dim=-1).detach().numpy(), atol=1e-12)
+
+
 BPINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -124,6 +144,17 @@ def test_pin(pin):
 
 
 # ---- planted mistakes -----------------------------------------------------
+
+def test_grads_at_matches_full_oracle():
+    """The row-sampled form equals attention_grads on the same sequence."""
+    n, d = 50, 6
+    q, k, v, do = _rand((n, d)), _rand((n, d)), _rand((n, d)), _rand((n, d))
+    rows = [0, 13, 49]
+    for causal in (False, True):
+        fq, fk, fv = ob._sequence_grads(q, k, v, do, 0.5, causal)
+        dq, dk, dv, _ = ob.grads_at(q, k, v, do, 0.5, causal, rows, rows, chunk=16)
+        assert np.allclose(dq, fq[rows]) and np.allclose(dk, fk[rows]) and np.allclose(dv, fv[rows])
+
 
 def _mutant(kind):
     def grads(q, k, v, do, scale, causal):
