@@ -212,3 +212,34 @@ def test_mxfp8_kernel_name():
     import io_aware_exact_attn_amd as ia
     assert ia.attn_kernel_name(128, 1, 1, 0, fp8=2) == "attn_fwd_fp8_kernel<causal,packed,mx>"
     assert ia.attn_kernel_name(64, 1, 0, 0, fp8=2) == ""
+
+
+def test_mxfp8_workload_sampled_rows():
+    """The shape and inputs `bench.py --extra mxfp8` times: the fp8
+    workload's bf16 q, k, v ([2, 8192, 16, 128], 1% +-20 outliers in all
+    three) quantised to MXFP8 on the GPU, causal; sampled query rows of two
+    (sequence, head) pairs against the oracle on the dequantised operands."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    w = W.workload(5)
+    B, N, H, d = w.B, w.N, w.H, w.d
+    shape = (B, N, H, d)
+    bits = [W.normal_bf16(W.tensor_seed(5, t), shape, True) for t in ("q", "k", "v")]
+    ys = [torch.empty(shape, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    ss = [torch.empty((B, N, H, d // 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ss.append(torch.empty((B, H, N // 32, d), dtype=torch.uint8, device="cuda"))
+    for i in range(3):
+        ia.attn_quantize_mxfp8(to_dev(bits[i]), ys[i], ss[i], B, H, N, d, None, int(i == 2))
+    o = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ia.attn_fwd_mxfp8(ys[0], ys[1], ys[2], ss[0], ss[1], ss[2], o, lse, B, H, N, d, w.scale, 1)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 31, 32, 127, 128, 2047, 4096, 6000, 8190, 8191])
+    for b, h in ((0, 3), (1, 14)):
+        qd = omx.dequantize_mx_d(ys[0][b:b + 1, :, h:h + 1].cpu().numpy(), ss[0][b:b + 1, :, h:h + 1].cpu().numpy())
+        kd = omx.dequantize_mx_d(ys[1][b:b + 1, :, h:h + 1].cpu().numpy(), ss[1][b:b + 1, :, h:h + 1].cpu().numpy())
+        vd = omx.dequantize_mx_tokens(ys[2][b:b + 1, :, h:h + 1].cpu().numpy(), ss[2][b:b + 1, h:h + 1].cpu().numpy())
+        Or, Lr = oracle.attention_rows(qd, kd, vd, w.scale, True, 0, 0, rows)
+        og = o[b, rows, h].float().cpu().numpy().astype(np.float64)
+        lg = lse[b, h, rows].cpu().numpy().astype(np.float64)
+        assert_within(errors(og, Or, lg, Lr), TOL_MX_ALL_OUTLIERS)

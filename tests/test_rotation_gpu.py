@@ -157,3 +157,15 @@ def test_rotation_reduces_fp8_error(mag, nch):
     print(f"plain fp8: mean {e0.mean():.5f} max {e0.max():.4f} lse {l0:.4f}; "
           f"rotated: mean {e1.mean():.5f} max {e1.max():.4f} lse {l1:.4f}")
     assert e1.mean() < e0.mean() and e1.max() < e0.max() and l1 < l0
+
+
+def test_rotated_quantize_workload_tensor():
+    """The whole q tensor `bench.py --extra rotate` rotates ([2, 8192, 16,
+    128] bf16, 1% +-20 outliers, its seeded signs), bit for bit."""
+    shape = (2, 8192, 16, 128)
+    bits = W.normal_bf16(7100, shape, True)
+    signs = W.random_signs(7102, 128)
+    y, s = run_rot(bits, signs)
+    yr, sr = orot.rotate_quantize_blocks(oracle.bf16_decode(bits), signs)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(y, yr)
