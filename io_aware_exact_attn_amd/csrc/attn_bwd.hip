@@ -256,9 +256,14 @@ bwd_dq_kernel(BwdArgs a) {
 // dK, dV: key blocks outer, query tiles inner
 // ---------------------------------------------------------------------------
 
-template <int D, bool CAUSAL, bool PACKED>
-__global__ void __launch_bounds__(bwd::NW * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
+// PART 0: dK and dV together; 1: dK only (S, dP, dK); 2: dV only (S, dV).
+// With both, d = 128 keeps K, V and two accumulators live (one wave per
+// SIMD); apart, each kernel fits two waves per SIMD for one more product.
+template <int D, bool CAUSAL, bool PACKED, int PART>
+__global__ void __launch_bounds__(bwd::NW * 64)
+__attribute__((amdgpu_waves_per_eu(D == 64 || PART != 0 ? 2 : 1, D == 64 || PART != 0 ? 2 : 1)))
 bwd_dkdv_kernel(BwdArgs a) {
+  constexpr bool DK = PART != 2, DV = PART != 1;
   using namespace bwd;
   constexpr int ROWB = D * 2, TILE = BN * ROWB;
   constexpr int CPW = TILE / 1024 / NW;
@@ -288,9 +293,9 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int key = wk0 + l32;
   const bool kok = key < seq_len;
   const int64_t krow = (int64_t)(seq_start + (kok ? key : 0)) * rs + head_off;
-  bf16x8 kf[DC], vf[DC];
+  bf16x8 kf[DC], vf[DK ? DC : 1];
   load_row_frags<D>((const uint16_t*)a.k + krow, rs, kok, hl, kf);
-  load_row_frags<D>((const uint16_t*)a.v + krow, rs, kok, hl, vf);
+  if constexpr (DK) load_row_frags<D>((const uint16_t*)a.v + krow, rs, kok, hl, vf);
 
   uint32_t lane_off[CPW];
 #pragma unroll
@@ -319,7 +324,7 @@ bwd_dkdv_kernel(BwdArgs a) {
                                                16, lane_off[cc] - cc * 1024, 0, cc * 1024, 0);
     });
     // the tile's L and D: one dword per lane (rows past the end read as 0)
-    if (wave < 2) {
+    if (wave < (DK ? 2 : 1)) {
       const float* src = wave == 0 ? a.lse : a.delta;
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(src + lrow + q0), (short)0, nrows * 4, kBufferFlags);
@@ -347,9 +352,12 @@ bwd_dkdv_kernel(BwdArgs a) {
       }
   }
 
-  f32x16 dkacc[DB], dvacc[DB];
+  f32x16 dkacc[DK ? DB : 1], dvacc[DV ? DB : 1];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) dkacc[db] = dvacc[db] = (f32x16){};
+  for (int db = 0; db < DB; ++db) {
+    if constexpr (DK) dkacc[db] = (f32x16){};
+    if constexpr (DV) dvacc[db] = (f32x16){};
+  }
 
   if (j_begin < j_end) issue_tile(0, j_begin);
   for (int j = j_begin; j < j_end; ++j) {
@@ -369,13 +377,15 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       __builtin_amdgcn_sched_barrier(0);       // one half's loads at a time: fewer live registers
-      f32x16 s, dp;
+      f32x16 s, dp = {};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const bf16x8 qfr = *(const bf16x8*)(qt + qb * 32 * ROWB + qoff[dc]);
-        const bf16x8 dfr = *(const bf16x8*)(dt + qb * 32 * ROWB + qoff[dc]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr, kf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
+        if constexpr (DK) {
+          const bf16x8 dfr = *(const bf16x8*)(dt + qb * 32 * ROWB + qoff[dc]);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
+        }
       }
       // query of register r: q0 + qb*32 + (r/4)*8 + hl*4 + r%4; its L and D
       // come from the tile's LDS rows, four at a time.  P goes to s, dS to dp.
@@ -383,14 +393,14 @@ bwd_dkdv_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int qi = qb * 32 + g * 8 + hl * 4;
         const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
-        const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
+        const f32x4 d4 = DK ? *(const f32x4*)(dlt_t + P * BN + qi) : (f32x4){};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = g * 4 + i;
           float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
           if (qi + i < lo || qi + i > hi) p = 0.f;
           s[r] = p;
-          dp[r] = p * (dp[r] - d4[i]);
+          if constexpr (DK) dp[r] = p * (dp[r] - d4[i]);
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time
@@ -409,21 +419,25 @@ bwd_dkdv_kernel(BwdArgs a) {
         const char* qq = qt + kc * 16 * ROWB;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x4 dlo = ds_read_tr16(dd + voff[0][db]);
-          const bf16x4 dhi = ds_read_tr16(dd + voff[1][db]);
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                              pf, dvacc[db], 0, 0, 0);
-          const bf16x4 qlo = ds_read_tr16(qq + voff[0][db]);
-          const bf16x4 qhi = ds_read_tr16(qq + voff[1][db]);
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                              dsf, dkacc[db], 0, 0, 0);
+          if constexpr (DV) {
+            const bf16x4 dlo = ds_read_tr16(dd + voff[0][db]);
+            const bf16x4 dhi = ds_read_tr16(dd + voff[1][db]);
+            dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7), pf, dvacc[db], 0, 0, 0);
+          }
+          if constexpr (DK) {
+            const bf16x4 qlo = ds_read_tr16(qq + voff[0][db]);
+            const bf16x4 qhi = ds_read_tr16(qq + voff[1][db]);
+            dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), dsf, dkacc[db], 0, 0, 0);
+          }
         }
       }
     }
   }
   if (kok) {
-    store_row<D>((uint16_t*)a.dk + krow, dkacc, a.scale, hl);
-    store_row<D>((uint16_t*)a.dv + krow, dvacc, 1.f, hl);
+    if constexpr (DK) store_row<D>((uint16_t*)a.dk + krow, dkacc, a.scale, hl);
+    if constexpr (DV) store_row<D>((uint16_t*)a.dv + krow, dvacc, 1.f, hl);
   }
 }
 
@@ -455,7 +469,13 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<D, CAUSAL, PACKED>), dim3(grid),
                                  dim3(bwd::NW * 64), args, 0, st);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, PACKED>), dim3(grid),
+  if constexpr (D == 64)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, PACKED, 0>), dim3(grid),
+                           dim3(bwd::NW * 64), args, 0, st);
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, PACKED, 1>), dim3(grid),
+                      dim3(bwd::NW * 64), args, 0, st);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, PACKED, 2>), dim3(grid),
                          dim3(bwd::NW * 64), args, 0, st);
 }
 
