@@ -376,7 +376,8 @@ bwd_dkdv_kernel(BwdArgs a) {
     // products into dV and dK, so only one half's scores are live at a time
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      __builtin_amdgcn_sched_barrier(0);       // one half's loads at a time: fewer live registers
+      if constexpr (PART == 0)
+        __builtin_amdgcn_sched_barrier(0);     // one half's loads at a time: fewer live registers
       f32x16 s, dp = {};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
