@@ -166,53 +166,67 @@ __global__ void __launch_bounds__(qz::NT) quantize_fp8_kernel(QuantArgs a) {
 // then runs on those fp32 values.
 //
 // MI355X mapping: one workgroup per 128-token block as above; a token row is
-// spread over D / 16 lanes, 16 coordinates each (two 16-byte loads), and the
-// transform is the in-place fast Walsh-Hadamard butterfly: four stages inside
-// the lane's registers, then log2(D / 16) stages across the row's lanes with
-// xor shuffles.  The block maximum is taken on the fp32 bit patterns.
+// spread over D / 32 lanes of one quad, 32 coordinates each (four 16-byte
+// loads), and the transform is the in-place fast Walsh-Hadamard butterfly:
+// five stages inside the lane's registers, then log2(D / 32) stages across
+// the row's lanes by DPP quad permutations (no LDS traffic).  The block
+// maximum is taken on the fp32 bit patterns.
 // ---------------------------------------------------------------------------
+// v from the lane whose index differs in the bit(s) of the quad permutation
+// CTRL (DPP, within each group of four lanes), for a double as two dwords
+template <int CTRL>
+__device__ __forceinline__ double dpp_swap(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 template <int D, bool PACKED>
 __global__ void __launch_bounds__(qz::NT) quantize_fp8_rot_kernel(QuantArgs a) {
-  constexpr int LPR = D / 16;                 // lanes per token row
+  constexpr int EPL = 32;                     // coordinates per lane
+  constexpr int LPR = D / EPL;                // lanes per token row: 4 (d = 128) or 2 (d = 64)
   constexpr int RPP = qz::NT / LPR;           // token rows per pass
   constexpr int NP = qz::BLK / RPP;           // passes per block
   const int tid = threadIdx.x;
-  const int li = tid % LPR;                   // this lane's 16 coordinates: li * 16 ...
+  const int li = tid % LPR;                   // this lane's coordinates: li * 32 ...
   const int64_t rs = (int64_t)a.H * D;
   QItem it;
   if (!q_item<PACKED>(a, blockIdx.x, D, it)) return;
   const uint16_t* __restrict__ x = (const uint16_t*)a.x + it.base;
   uint8_t* __restrict__ y = (uint8_t*)a.y + it.base;
 
-  u32x4 raw[NP][2];
+  u32x4 raw[NP][4];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int row = p * RPP + tid / LPR;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-      raw[p][c] = row < it.nt ? *(const u32x4*)(x + row * rs + li * 16 + c * 8) : (u32x4){0u, 0u, 0u, 0u};
+    for (int c = 0; c < 4; ++c)
+      raw[p][c] = row < it.nt ? *(const u32x4*)(x + row * rs + li * EPL + c * 8) : (u32x4){0u, 0u, 0u, 0u};
   }
   // sign flips as xor masks on the bf16 pairs: word w of chunk c holds
   // coordinates 8c + 2w (low half) and 8c + 2w + 1 (high half)
-  const u32x4 sg = *(const u32x4*)(a.signs + li * 16);
-  uint32_t flip[2][4];
+  const u32x4 sg0 = *(const u32x4*)(a.signs + li * EPL);
+  const u32x4 sg1 = *(const u32x4*)(a.signs + li * EPL + 16);
+  uint32_t flip[4][4];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int e0 = 8 * c + 2 * w, e1 = e0 + 1;
-      const uint32_t b0 = (sg[e0 >> 2] >> ((e0 & 3) * 8 + 7)) & 1u;
-      const uint32_t b1 = (sg[e1 >> 2] >> ((e1 & 3) * 8 + 7)) & 1u;
+      const uint32_t s0 = (e0 < 16 ? sg0 : sg1)[(e0 & 15) >> 2], s1 = (e1 < 16 ? sg0 : sg1)[(e1 & 15) >> 2];
+      const uint32_t b0 = (s0 >> ((e0 & 3) * 8 + 7)) & 1u;
+      const uint32_t b1 = (s1 >> ((e1 & 3) * 8 + 7)) & 1u;
       flip[c][w] = (b0 << 15) | (b1 << 31);
     }
 
-  float r[NP][16];
+  float r[NP][EPL];
   uint32_t mb = 0;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    double v[16];
+    double v[EPL];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t u = raw[p][c][w] ^ flip[c][w];
@@ -220,25 +234,34 @@ __global__ void __launch_bounds__(qz::NT) quantize_fp8_rot_kernel(QuantArgs a) {
         v[8 * c + 2 * w + 1] = (double)__uint_as_float(u & 0xffff0000u);
       }
 #pragma unroll
-    for (int hb = 1; hb < 16; hb <<= 1)
+    for (int hb = 1; hb < EPL; hb <<= 1)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
+      for (int e = 0; e < EPL; ++e)
         if (!(e & hb)) {
           const double s0 = v[e], s1 = v[e + hb];
           v[e] = s0 + s1;
           v[e + hb] = s0 - s1;
         }
+    // the row's other lanes: xor 1 (quad permutation 1 0 3 2), then xor 2
+    // (2 3 0 1) for d = 128
+    {
+      const bool upper = (li & 1) != 0;
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) {
-      const bool upper = (li & m) != 0;
+      for (int e = 0; e < EPL; ++e) {
+        const double o = dpp_swap<0xB1>(v[e]);
+        v[e] = upper ? o - v[e] : v[e] + o;
+      }
+    }
+    if constexpr (LPR == 4) {
+      const bool upper = (li & 2) != 0;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const double o = __shfl_xor(v[e], m);
+      for (int e = 0; e < EPL; ++e) {
+        const double o = dpp_swap<0x4E>(v[e]);
         v[e] = upper ? o - v[e] : v[e] + o;
       }
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < EPL; ++e) {
       r[p][e] = (float)(v[e] + 0.0);          // + 0.0: an exact zero sum becomes +0
       mb = max(mb, __float_as_uint(r[p][e]) & 0x7fffffffu);
     }
@@ -264,14 +287,18 @@ __global__ void __launch_bounds__(qz::NT) quantize_fp8_rot_kernel(QuantArgs a) {
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int row = p * RPP + tid / LPR;
-    u32x4 out;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(quot(r[p][4 * w]), quot(r[p][4 * w + 1]), 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(quot(r[p][4 * w + 2]), quot(r[p][4 * w + 3]), word, true);
-      out[w] = (uint32_t)word;
+    for (int c = 0; c < 2; ++c) {
+      u32x4 out;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int e = 16 * c + 4 * w;
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(quot(r[p][e]), quot(r[p][e + 1]), 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(quot(r[p][e + 2]), quot(r[p][e + 3]), word, true);
+        out[w] = (uint32_t)word;
+      }
+      if (row < it.nt) *(u32x4*)(y + row * rs + li * EPL + 16 * c) = out;
     }
-    if (row < it.nt) *(u32x4*)(y + row * rs + li * 16) = out;
   }
 }
 
