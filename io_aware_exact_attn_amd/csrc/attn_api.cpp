@@ -104,8 +104,10 @@ ATTN_API int attn_fwd_mxfp8(const void* q, const void* k, const void* v, const u
   if (!aligned16(q_scale) || !aligned16(k_scale) || !aligned16(v_scale)) return ATTN_ERR_ALIGN;
   if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
   if (cu_seqlens && (int64_t)H * ((N + 127) / 128 + B) + 8 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-  // V scale rows: ceil(N / 32) blocks per (sequence, head), packed + B
-  if ((int64_t)H * B * ((N + 31) / 32 + 1) * d >= ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;
+  // V scale slots per head row (ceil(N / 32), packed + B) are int; a tile's K
+  // scale bytes (64 tokens x H x 4) are addressed with 32-bit offsets
+  if ((int64_t)H * ((N + 31) / 32 + (cu_seqlens ? B : 0)) >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  if ((int64_t)64 * H * 4 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
   a.q_scale = reinterpret_cast<const float*>(q_scale);
   a.k_scale = reinterpret_cast<const float*>(k_scale);
   a.v_scale = reinterpret_cast<const float*>(v_scale);

@@ -87,6 +87,28 @@ def test_attn_fwd_fp8_rejects(kw, status):
     assert fp8(**kw) == status
 
 
+def mxfp8(**kw):
+    args = dict(q=P, k=P, v=P, q_scale=P, k_scale=P, v_scale=P, o=P, lse=P, B=1, H=1, N=128,
+                d=128, scale=0.1, causal=1, cu_seqlens=None, stream=0)
+    args.update(kw)
+    return ia.attn_fwd_mxfp8(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ia.ATTN_ERR_NULL), (dict(k_scale=None), ia.ATTN_ERR_NULL), (dict(v_scale=None), ia.ATTN_ERR_NULL),
+    (dict(lse=None), ia.ATTN_ERR_NULL),
+    (dict(d=64), ia.ATTN_ERR_UNSUPPORTED), (dict(causal=3), ia.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), ia.ATTN_ERR_SCALE),
+    (dict(q_scale=MIS), ia.ATTN_ERR_ALIGN), (dict(v_scale=MIS), ia.ATTN_ERR_ALIGN), (dict(o=MIS), ia.ATTN_ERR_ALIGN),
+    (dict(cu_seqlens=MIS), ia.ATTN_ERR_ALIGN),
+    (dict(N=0), ia.ATTN_ERR_SHAPE), (dict(B=1 << 16, H=1 << 8, N=1 << 8), ia.ATTN_ERR_SHAPE),
+    (dict(cu_seqlens=P, B=1 << 30, H=4, N=1), ia.ATTN_ERR_SHAPE),
+    (dict(H=(1 << 17) + 1, N=1), ia.ATTN_ERR_SHAPE),     # H * d > 2^24
+])
+def test_attn_fwd_mxfp8_rejects(kw, status):
+    assert mxfp8(**kw) == status
+
+
 def quant(**kw):
     args = dict(x=P, y=P, scales=P, B=1, H=2, N=300, d=128, cu_seqlens=None, stream=0)
     args.update(kw)
