@@ -118,8 +118,10 @@ def mx_chain(q, k, v, scale, causal, cu=None):
     for x, tokens in ((q, False), (k, False), (v, True)):
         y = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
         if tokens:
-            s = torch.zeros((H, -(-N // 32) + B, d) if packed else (B, H, -(-N // 32), d), dtype=torch.uint8,
-                            device="cuda")
+            # 0xFF is E8M0's NaN: packed slots no block maps to keep it, and
+            # the kernel must never read them
+            s = torch.full((H, -(-N // 32) + B, d) if packed else (B, H, -(-N // 32), d), 0xFF, dtype=torch.uint8,
+                           device="cuda")
         else:
             s = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device="cuda")
         ia.attn_quantize_mxfp8(to_dev(x), y, s, B, H, N, d, cud, int(tokens))
