@@ -79,11 +79,17 @@ FWD_SOURCES = ("attn_fwd_bf16.hip", "attn_common.h", "attn_kernels.h")
 
 
 def source_hash():
+    """Hash of those sources with comments and blank space removed, so that
+    only a change to the code itself invalidates the counters."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "io_aware_exact_attn_amd", "csrc")
     for name in FWD_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -36,14 +36,15 @@ struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
-  const float* q_scale;      // fp8 only: [B][H][nsb]
-  const float* k_scale;
-  const float* v_scale;
+  const float* q_scale;      // fp8: fp32 [B][H][nsb]; MXFP8: E8M0 bytes read through
+  const float* k_scale;      //   the same pointers (q, k [tokens][H][d / 32],
+  const float* v_scale;      //   v [rows of 32-token blocks][d]), cast back in the kernel
   void* o;
   float* lse;
   const int32_t* cu_seqlens; // packed documents, device, B + 1 entries
   int B, H, N;               // N: tokens per sequence, or total tokens when packed
-  int nsb;                   // fp8: scale blocks per sequence = ceil(N / 128)
+  int nsb;                   // fp8: scale blocks per sequence = ceil(N / 128) (packed + B);
+                             // MXFP8: V's 32-token blocks, ceil(N / 32) (packed + B)
   int slots;                 // workgroup slots per head (packed) or q blocks per sequence
   int n_work;                // number of real work items
   int per_xcd;               // grid / 8
@@ -77,7 +78,8 @@ struct BwdArgs {
 struct QuantArgs {
   const void* x;             // bf16 input, [B][N][H][d] or packed [N][H][d]
   void* y;                   // e4m3 output, same layout
-  float* scales;             // [B][H][nsb] or packed [H][nsb]
+  float* scales;             // [B][H][nsb] or packed [H][nsb]; the MXFP8 quantiser writes
+                             // E8M0 bytes through it (its own layouts)
   const int32_t* cu_seqlens; // packed documents, device, B + 1 entries
   const int8_t* signs;       // rotating quantiser: d random signs (+1 / -1), device
   int B, H, N;
