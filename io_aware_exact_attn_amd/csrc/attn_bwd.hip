@@ -17,7 +17,9 @@
 //   * dQ: one workgroup per 128 query rows walks the key/value tiles, as the
 //     forward does, with S^T = K Q^T and dP^T = V dO^T and dQ^T += K^T dS^T;
 //   * dK/dV: one workgroup per 128 keys walks the query tiles, with
-//     S = Q K^T and dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS.
+//     S = Q K^T and dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS (at
+//     d = 128 two waves share 32 keys, each forming S and dP for half of a
+//     query tile and accumulating half of the coordinates).
 // Splitting dQ from dK/dV recomputes S and dP once more but needs no atomics
 // and no fp32 accumulation buffer for dQ.
 //
@@ -256,14 +258,13 @@ bwd_dq_kernel(BwdArgs a) {
 // dK, dV: key blocks outer, query tiles inner
 // ---------------------------------------------------------------------------
 
-// PART 0: dK and dV together; 1: dK only (S, dP, dK); 2: dV only (S, dV).
-// With both, d = 128 keeps K, V and two accumulators live (one wave per
-// SIMD); apart, each kernel fits two waves per SIMD for one more product.
-template <int D, bool CAUSAL, bool PACKED, int PART>
-__global__ void __launch_bounds__(bwd::NW * 64)
-__attribute__((amdgpu_waves_per_eu(D == 64 || PART != 0 ? 2 : 1, D == 64 || PART != 0 ? 2 : 1)))
+// d = 64: K, V and both accumulators fit two waves per SIMD in one wave per
+// 32 keys.  (At d = 128 they keep about 192 VGPRs live; the wave-pair kernel
+// below splits the coordinates instead.)
+template <int D, bool CAUSAL, bool PACKED>
+__global__ void __launch_bounds__(bwd::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
-  constexpr bool DK = PART != 2, DV = PART != 1;
+  static_assert(D == 64, "d = 128 uses bwd_dkdv_pair_kernel");
   using namespace bwd;
   constexpr int ROWB = D * 2, TILE = BN * ROWB;
   constexpr int CPW = TILE / 1024 / NW;
@@ -293,9 +294,9 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int key = wk0 + l32;
   const bool kok = key < seq_len;
   const int64_t krow = (int64_t)(seq_start + (kok ? key : 0)) * rs + head_off;
-  bf16x8 kf[DC], vf[DK ? DC : 1];
+  bf16x8 kf[DC], vf[DC];
   load_row_frags<D>((const uint16_t*)a.k + krow, rs, kok, hl, kf);
-  if constexpr (DK) load_row_frags<D>((const uint16_t*)a.v + krow, rs, kok, hl, vf);
+  load_row_frags<D>((const uint16_t*)a.v + krow, rs, kok, hl, vf);
 
   uint32_t lane_off[CPW];
 #pragma unroll
@@ -324,7 +325,7 @@ bwd_dkdv_kernel(BwdArgs a) {
                                                16, lane_off[cc] - cc * 1024, 0, cc * 1024, 0);
     });
     // the tile's L and D: one dword per lane (rows past the end read as 0)
-    if (wave < (DK ? 2 : 1)) {
+    if (wave < 2) {
       const float* src = wave == 0 ? a.lse : a.delta;
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(src + lrow + q0), (short)0, nrows * 4, kBufferFlags);
@@ -352,12 +353,9 @@ bwd_dkdv_kernel(BwdArgs a) {
       }
   }
 
-  f32x16 dkacc[DK ? DB : 1], dvacc[DV ? DB : 1];
+  f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    if constexpr (DK) dkacc[db] = (f32x16){};
-    if constexpr (DV) dvacc[db] = (f32x16){};
-  }
+  for (int db = 0; db < DB; ++db) dkacc[db] = dvacc[db] = (f32x16){};
 
   if (j_begin < j_end) issue_tile(0, j_begin);
   for (int j = j_begin; j < j_end; ++j) {
@@ -376,17 +374,14 @@ bwd_dkdv_kernel(BwdArgs a) {
     // products into dV and dK, so only one half's scores are live at a time
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      if constexpr (PART == 0)
-        __builtin_amdgcn_sched_barrier(0);     // one half's loads at a time: fewer live registers
-      f32x16 s, dp = {};
+      __builtin_amdgcn_sched_barrier(0);       // one half's loads at a time: fewer live registers
+      f32x16 s, dp;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const bf16x8 qfr = *(const bf16x8*)(qt + qb * 32 * ROWB + qoff[dc]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr, kf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
-        if constexpr (DK) {
-          const bf16x8 dfr = *(const bf16x8*)(dt + qb * 32 * ROWB + qoff[dc]);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
-        }
+        const bf16x8 dfr = *(const bf16x8*)(dt + qb * 32 * ROWB + qoff[dc]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
       }
       // query of register r: q0 + qb*32 + (r/4)*8 + hl*4 + r%4; its L and D
       // come from the tile's LDS rows, four at a time.  P goes to s, dS to dp.
@@ -394,14 +389,14 @@ bwd_dkdv_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int qi = qb * 32 + g * 8 + hl * 4;
         const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
-        const f32x4 d4 = DK ? *(const f32x4*)(dlt_t + P * BN + qi) : (f32x4){};
+        const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = g * 4 + i;
           float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
           if (qi + i < lo || qi + i > hi) p = 0.f;
           s[r] = p;
-          if constexpr (DK) dp[r] = p * (dp[r] - d4[i]);
+          dp[r] = p * (dp[r] - d4[i]);
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time
@@ -420,25 +415,224 @@ bwd_dkdv_kernel(BwdArgs a) {
         const char* qq = qt + kc * 16 * ROWB;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          if constexpr (DV) {
-            const bf16x4 dlo = ds_read_tr16(dd + voff[0][db]);
-            const bf16x4 dhi = ds_read_tr16(dd + voff[1][db]);
-            dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7), pf, dvacc[db], 0, 0, 0);
-          }
-          if constexpr (DK) {
-            const bf16x4 qlo = ds_read_tr16(qq + voff[0][db]);
-            const bf16x4 qhi = ds_read_tr16(qq + voff[1][db]);
-            dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), dsf, dkacc[db], 0, 0, 0);
-          }
+          const bf16x4 dlo = ds_read_tr16(dd + voff[0][db]);
+          const bf16x4 dhi = ds_read_tr16(dd + voff[1][db]);
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7), pf, dvacc[db], 0, 0, 0);
+          const bf16x4 qlo = ds_read_tr16(qq + voff[0][db]);
+          const bf16x4 qhi = ds_read_tr16(qq + voff[1][db]);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), dsf, dkacc[db], 0, 0, 0);
         }
       }
     }
   }
   if (kok) {
-    if constexpr (DK) store_row<D>((uint16_t*)a.dk + krow, dkacc, a.scale, hl);
-    if constexpr (DV) store_row<D>((uint16_t*)a.dv + krow, dvacc, 1.f, hl);
+    store_row<D>((uint16_t*)a.dk + krow, dkacc, a.scale, hl);
+    store_row<D>((uint16_t*)a.dv + krow, dvacc, 1.f, hl);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV with wave pairs (d = 128): no recomputation at two waves per SIMD
+// ---------------------------------------------------------------------------
+
+// Eight waves per 128 keys, two per group of 32 keys.  Both waves of a pair
+// hold the group's K and V rows (all d) and split each 64-query tile: wave
+// half h forms S = Q K^T, dP = dO V^T, P and dS for queries 32 h .. 32 h + 31
+// and leaves its two 16-query chunks of P and dS, packed as the next
+// product's B operand, in LDS; after a barrier each wave takes its partner's
+// chunks and accumulates dV^T += dO^T P and dK^T += Q^T dS for all 64 queries
+// but only its own 64 of the 128 coordinates.
+template <int D, bool CAUSAL, bool PACKED>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_pair_kernel(BwdArgs a) {
+  using namespace bwd;
+  static_assert(D == 128, "wave pairs split d = 128 in two");
+  constexpr int NWP = 8;                       // waves per workgroup
+  constexpr int ROWB = D * 2, TILE = BN * ROWB;
+  constexpr int CPW = TILE / 1024 / NWP;       // 1 KB load chunks per wave per tile
+  constexpr int DC = D / 16, DBH = D / 64;     // k-steps of S; 32-wide d blocks per wave
+  // Q0 Q1 dO0 dO1 | L, D of both tiles | P, dS chunks [4 pairs][2 kinds][4 chunks][64 lanes][16 B]
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 4 * BN * 4 + 4 * 2 * 4 * 64 * 16];
+  float* lse_t = (float*)(smem + 4 * TILE);    // [2][BN]
+  float* dlt_t = lse_t + 2 * BN;               // [2][BN]
+  char* xch = smem + 4 * TILE + 4 * BN * 4;
+
+  int h, b, seq_start, seq_len, kblk;
+  if (!decode_work<BM, false, PACKED>(a, blockIdx.x, h, b, seq_start, seq_len, kblk)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave >> 1, half = wave & 1;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int k0 = kblk * BM, wk0 = k0 + pair * 32;
+  const int j_begin = CAUSAL ? k0 / BN : 0;
+  const int j_end = (seq_len + BN - 1) / BN;
+  const int pair_begin = CAUSAL ? wk0 / BN : 0;
+  const bool pair_live = wk0 < seq_len;
+  const int64_t rs = (int64_t)a.H * D;
+  const int64_t head_off = (int64_t)h * D;
+  [[maybe_unused]] const int64_t lrow = PACKED ? (int64_t)h * a.N + seq_start : (int64_t)(b * a.H + h) * a.N;
+
+  const int key = wk0 + l32;
+  const bool kok = key < seq_len;
+  const int64_t krow = (int64_t)(seq_start + (kok ? key : 0)) * rs + head_off;
+  bf16x8 kf[DC], vf[DC];
+  load_row_frags<D>((const uint16_t*)a.k + krow, rs, kok, hl, kf);
+  load_row_frags<D>((const uint16_t*)a.v + krow, rs, kok, hl, vf);
+
+  uint32_t lane_off[CPW];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    const int byte = (wave * CPW + cc) * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int gr = ((byte % ROWB) >> 4) ^ swz<D>(row);
+    lane_off[cc] = (uint32_t)(((int64_t)row * rs + head_off + gr * 8) * 2);
+  }
+  [[maybe_unused]] const uint32_t row_bytes = (uint32_t)rs * 2u;
+  auto issue_tile = [&](int buf, int j) __attribute__((always_inline)) {
+#if __HIP_DEVICE_COMPILE__
+    const int q0 = j * BN;
+    const int nrows = min(seq_len - q0, BN);
+    const uint32_t nrec = (uint32_t)nrows * row_bytes;
+    const uint64_t off = (uint64_t)(uint32_t)(seq_start + q0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)a.q + off), (short)0, (int)nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)a.dout + off), (short)0, (int)nrec, kBufferFlags);
+    static_for<CPW>([&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (IAEA_LDS void*)(smem + buf * TILE + wave * CPW * 1024),
+                                               16, lane_off[cc] - cc * 1024, 0, cc * 1024, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (IAEA_LDS void*)(smem + (2 + buf) * TILE + wave * CPW * 1024),
+                                               16, lane_off[cc] - cc * 1024, 0, cc * 1024, 0);
+    });
+    if (wave < 2) {
+      const float* src = wave == 0 ? a.lse : a.delta;
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(src + lrow + q0), (short)0, nrows * 4, kBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (IAEA_LDS void*)((wave == 0 ? lse_t : dlt_t) + buf * BN),
+                                               4, lane * 4, 0, 0, 0);
+    }
+#endif
+  };
+
+  uint32_t qoff[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) qoff[dc] = l32 * ROWB + (((2 * dc + hl) ^ swz<D>(l32)) << 4);
+  uint32_t voff[2][DBH];
+  {
+    const int g16 = lane >> 4;
+    const int v_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+    const int v_dcol = 16 * (g16 & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int dbl = 0; dbl < DBH; ++dbl) {
+        const int row = v_row + 8 * hi;
+        const int d = (half * DBH + dbl) * 32 + v_dcol;
+        voff[hi][dbl] = row * ROWB + (((d >> 3) ^ swz<D>(row)) << 4) + (d & 7) * 2;
+      }
+  }
+  // this pair's exchange slots: kind 0 = P, 1 = dS; chunk kc of the tile
+  char* const pxch = xch + pair * (2 * 4 * 64 * 16);
+  auto slot = [&](int kind, int kc) __attribute__((always_inline)) -> char* {
+    return pxch + ((kind * 4 + kc) * 64 + lane) * 16;
+  };
+
+  f32x16 dkacc[DBH], dvacc[DBH];
+#pragma unroll
+  for (int dbl = 0; dbl < DBH; ++dbl) dkacc[dbl] = dvacc[dbl] = (f32x16){};
+
+  if (j_begin < j_end) issue_tile(0, j_begin);
+  for (int j = j_begin; j < j_end; ++j) {
+    const int P = (j - j_begin) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                           // tile j landed; last tile's chunks all read
+    if (j + 1 < j_end) issue_tile(P ^ 1, j + 1);
+    const bool live = pair_live && j >= pair_begin;
+    const char* qt = smem + P * TILE;
+    const char* dt = smem + (2 + P) * TILE;
+    const int q0 = j * BN;
+    bf16x8 own_p[2], own_ds[2];
+    if (live) {
+      // S and dP of this wave's 32 queries (rows 32 half .. of the tile)
+      f32x16 s, dp;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 qfr = *(const bf16x8*)(qt + half * 32 * ROWB + qoff[dc]);
+        const bf16x8 dfr = *(const bf16x8*)(dt + half * 32 * ROWB + qoff[dc]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr, kf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
+      }
+      const int lo = CAUSAL ? key - q0 : 0;
+      const int hi = kok ? seq_len - 1 - q0 : -1;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = half * 32 + g * 8 + hl * 4;
+        const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
+        const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = g * 4 + i;
+          float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
+          if (qi + i < lo || qi + i > hi) p = 0.f;
+          s[r] = p;
+          dp[r] = p * (dp[r] - d4[i]);
+        }
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 pw, dw;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          pw[jj] = pack_bf16x2(s[8 * c2 + 2 * jj], s[8 * c2 + 2 * jj + 1]);
+          dw[jj] = pack_bf16x2(dp[8 * c2 + 2 * jj], dp[8 * c2 + 2 * jj + 1]);
+        }
+        own_p[c2] = __builtin_bit_cast(bf16x8, pw);
+        own_ds[c2] = __builtin_bit_cast(bf16x8, dw);
+        *(u32x4*)slot(0, half * 2 + c2) = pw;
+        *(u32x4*)slot(1, half * 2 + c2) = dw;
+      }
+    }
+    __syncthreads();                           // both halves' chunks in LDS
+    if (!live) continue;
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's four 16-query chunks,
+    // this wave's 64 coordinates
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bool mine = (kc >> 1) == half;
+      const bf16x8 pf = mine ? own_p[kc & 1] : *(const bf16x8*)slot(0, kc);
+      const bf16x8 dsf = mine ? own_ds[kc & 1] : *(const bf16x8*)slot(1, kc);
+      const char* dd = dt + kc * 16 * ROWB;
+      const char* qq = qt + kc * 16 * ROWB;
+#pragma unroll
+      for (int dbl = 0; dbl < DBH; ++dbl) {
+        const bf16x4 dlo = ds_read_tr16(dd + voff[0][dbl]);
+        const bf16x4 dhi = ds_read_tr16(dd + voff[1][dbl]);
+        dvacc[dbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7), pf, dvacc[dbl], 0, 0, 0);
+        const bf16x4 qlo = ds_read_tr16(qq + voff[0][dbl]);
+        const bf16x4 qhi = ds_read_tr16(qq + voff[1][dbl]);
+        dkacc[dbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), dsf, dkacc[dbl], 0, 0, 0);
+      }
+    }
+  }
+  if (kok) {
+    // this wave's 64 coordinates of the key's dK and dV rows
+#pragma unroll
+    for (int dbl = 0; dbl < DBH; ++dbl)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = (half * DBH + dbl) * 32 + g * 8 + hl * 4;
+        *(u32x2*)((uint16_t*)a.dk + krow + d) =
+            (u32x2){pack_bf16x2(dkacc[dbl][g * 4 + 0] * a.scale, dkacc[dbl][g * 4 + 1] * a.scale),
+                    pack_bf16x2(dkacc[dbl][g * 4 + 2] * a.scale, dkacc[dbl][g * 4 + 3] * a.scale)};
+        *(u32x2*)((uint16_t*)a.dv + krow + d) =
+            (u32x2){pack_bf16x2(dvacc[dbl][g * 4 + 0], dvacc[dbl][g * 4 + 1]),
+                    pack_bf16x2(dvacc[dbl][g * 4 + 2], dvacc[dbl][g * 4 + 3])};
+      }
   }
 }
 
@@ -471,13 +665,11 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
                                  dim3(bwd::NW * 64), args, 0, st);
   if (e != hipSuccess) return e;
   if constexpr (D == 64)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, PACKED, 0>), dim3(grid),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, PACKED>), dim3(grid),
                            dim3(bwd::NW * 64), args, 0, st);
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, PACKED, 1>), dim3(grid),
-                      dim3(bwd::NW * 64), args, 0, st);
-  if (e != hipSuccess) return e;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, PACKED, 2>), dim3(grid),
-                         dim3(bwd::NW * 64), args, 0, st);
+  else
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_pair_kernel<D, CAUSAL, PACKED>), dim3(grid),
+                           dim3(512), args, 0, st);
 }
 
 template <int D>
