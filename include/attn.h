@@ -170,8 +170,9 @@ ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
  *   dout        bf16 dO, layout of o.
  *   delta       fp32 workspace with the layout of lse, owned by the caller;
  *               on return it holds D (rowsum of dO * O).
- *   dq, dk, dv  bf16 outputs, layout of q; fully overwritten (dq may not alias
- *               any input).
+ *   dq, dk, dv  bf16 outputs, layout of q; fully overwritten.  None of them
+ *               may alias an input, delta or each other (other workgroups are
+ *               still reading the inputs while a gradient row is written).
  *   d in {64, 128}.  Errors as attn_fwd.  The three kernels are enqueued on
  *   `stream` in order (D, then dQ, then dK and dV).
  */
