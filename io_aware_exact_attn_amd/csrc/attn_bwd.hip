@@ -146,6 +146,8 @@ bwd_dq_kernel(BwdArgs a) {
   load_row_frags<D>((const uint16_t*)a.dout + trow, rs, tok, hl, df);
   const float lse2 = tok ? a.lse[lrow + t] * kLog2e : 0.f;
   const float dlt = tok ? a.delta[lrow + t] : 0.f;
+  // every lane's last visible key is at least this one
+  const int vis_lo = CAUSAL ? min(wq0, seq_len - 1) : seq_len - 1;
 
   // tile loads
   uint32_t lane_off[CPW];
@@ -225,14 +227,21 @@ bwd_dq_kernel(BwdArgs a) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, df[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
       }
-      // P^T and dS^T in place; key of register r: kv0 + kb*32 + (r/4)*8 + hl*4 + r%4
+      // P^T and dS^T in place; key of register r: kv0 + kb*32 + (r/4)*8 + hl*4 + r%4.
+      // The mask is applied only where some key of the half lies past the
+      // wave's first query (causal) or the sequence end.
       const int lim = (CAUSAL ? min(t, seq_len - 1) : seq_len - 1) - (kv0 + kb * 32 + hl * 4);
+      auto weights = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[r], a.c, -lse2));
-        if ((r >> 2) * 8 + (r & 3) > lim) p = 0.f;
-        s[r] = p * (dp[r] - dlt);
-      }
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], a.c, -lse2));
+          if constexpr (decltype(masked)::value)
+            if ((r >> 2) * 8 + (r & 3) > lim) p = 0.f;
+          s[r] = p * (dp[r] - dlt);
+        }
+      };
+      if (vis_lo >= kv0 + kb * 32 + 31) weights(std::false_type{});
+      else weights(std::true_type{});
       // dQ^T += K^T dS^T, 16 keys at a time
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
@@ -385,20 +394,28 @@ bwd_dkdv_kernel(BwdArgs a) {
       }
       // query of register r: q0 + qb*32 + (r/4)*8 + hl*4 + r%4; its L and D
       // come from the tile's LDS rows, four at a time.  P goes to s, dS to dp.
+      auto weights = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qi = qb * 32 + g * 8 + hl * 4;
-        const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
-        const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
+        for (int g = 0; g < 4; ++g) {
+          const int qi = qb * 32 + g * 8 + hl * 4;
+          const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
+          const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = g * 4 + i;
-          float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
-          if (qi + i < lo || qi + i > hi) p = 0.f;
-          s[r] = p;
-          dp[r] = p * (dp[r] - d4[i]);
+          for (int i = 0; i < 4; ++i) {
+            const int r = g * 4 + i;
+            float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
+            if constexpr (decltype(masked)::value)
+              if (qi + i < lo || qi + i > hi) p = 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[i]);
+          }
         }
-      }
+      };
+      // the mask only where the half's queries meet the diagonal or a tail
+      if ((!CAUSAL || q0 + qb * 32 >= wk0 + 31) && q0 + qb * 32 + 32 <= seq_len && wk0 + 32 <= seq_len)
+        weights(std::false_type{});
+      else
+        weights(std::true_type{});
       // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
@@ -567,20 +584,28 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
       }
       const int lo = CAUSAL ? key - q0 : 0;
       const int hi = kok ? seq_len - 1 - q0 : -1;
+      auto weights = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qi = half * 32 + g * 8 + hl * 4;
-        const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
-        const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
+        for (int g = 0; g < 4; ++g) {
+          const int qi = half * 32 + g * 8 + hl * 4;
+          const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
+          const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = g * 4 + i;
-          float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
-          if (qi + i < lo || qi + i > hi) p = 0.f;
-          s[r] = p;
-          dp[r] = p * (dp[r] - d4[i]);
+          for (int i = 0; i < 4; ++i) {
+            const int r = g * 4 + i;
+            float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
+            if constexpr (decltype(masked)::value)
+              if (qi + i < lo || qi + i > hi) p = 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[i]);
+          }
         }
-      }
+      };
+      // the mask only where this wave's queries meet the diagonal or a tail
+      if ((!CAUSAL || q0 + half * 32 >= wk0 + 31) && q0 + half * 32 + 32 <= seq_len && wk0 + 32 <= seq_len)
+        weights(std::false_type{});
+      else
+        weights(std::true_type{});
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         u32x4 pw, dw;
