@@ -193,3 +193,31 @@ def test_packed_fp8_causal_scale_safety():
     assert np.array_equal(O1[:blk], O2[:blk]) and np.array_equal(L1[:, :blk], L2[:, :blk])
     assert np.array_equal(O1[int(cu[2]):], O2[int(cu[2]):])
     assert not np.array_equal(O1[blk:int(cu[2])], O2[blk:int(cu[2])])
+
+
+def test_packed_workload_fp8_sampled():
+    """The packed-document workload (26 documents, 32768 tokens, H 16, d 128)
+    as `bench.py --extra fp8_packed` runs it: bf16 Q, K and V quantised by
+    attn_quantize_fp8 with document-local scales, then attn_fwd_fp8 with
+    cu_seqlens.  Rows of the longest and of a median-length document, in the
+    first and last heads, against the oracle on the operands of the oracle's
+    own quantiser, applied to each sampled document alone."""
+    w = W.workload(4)
+    inp = W.make_inputs(w)
+    cu = [int(c) for c in inp["cu_seqlens"]]
+    gpu = [run_quant(inp[t], cu) for t in ("q", "k", "v")]
+    O, L = run_fp8_packed(*[y for y, _ in gpu], *[s for _, s in gpu], cu, w.scale, 1)
+    lens = np.diff(cu)
+    Os, Or, Ls, Lr = [], [], [], []
+    for doc, h in ((int(np.argmax(lens)), 0), (int(np.argsort(lens)[len(lens) // 2]), w.H - 1)):
+        # documents are independent: the oracle takes this one on its own
+        a, n = cu[doc], int(lens[doc])
+        one = [0, n]
+        deq = [oq.dequantize_blocks(*oracle_quant(inp[t][a:a + n], one), one) for t in ("q", "k", "v")]
+        local = np.unique(np.clip([0, 1, 63, 64, 127, 128, 129, n // 3, n // 2, n - 2, n - 1], 0, n - 1))
+        o_ref, l_ref = oracle.attention_rows(*deq, w.scale, True, 0, h, local, cu_seqlens=one)
+        Os.append(O[a + local, h]); Or.append(o_ref); Ls.append(L[h, a + local]); Lr.append(l_ref)
+    err = errors(np.concatenate(Os), np.concatenate(Or), np.concatenate(Ls), np.concatenate(Lr), out="bf16")
+    print("packed workload fp8", err)
+    assert_within(err, TOL_FP8)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
