@@ -30,6 +30,8 @@
 // (buffer_load_dwordx4 ... lds); P and dS are rounded to bf16 and reused as
 // the B operand of the next product in the accumulator's own register order,
 // with the A operand read in the matching order by ds_read_b64_tr_b16.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_kernels.h"
 
