@@ -34,6 +34,7 @@
 
 #include "attn_common.h"
 #include "attn_kernels.h"
+#include "attn_mask.h"
 
 namespace iaea {
 
@@ -148,8 +149,6 @@ bwd_dq_kernel(BwdArgs a) {
   load_row_frags<D>((const uint16_t*)a.dout + trow, rs, tok, hl, df);
   const float lse2 = tok ? a.lse[lrow + t] * kLog2e : 0.f;
   const float dlt = tok ? a.delta[lrow + t] : 0.f;
-  // every lane's last visible key is at least this one
-  const int vis_lo = CAUSAL ? min(wq0, seq_len - 1) : seq_len - 1;
 
   // tile loads
   uint32_t lane_off[CPW];
@@ -242,7 +241,7 @@ bwd_dq_kernel(BwdArgs a) {
           s[r] = p * (dp[r] - dlt);
         }
       };
-      if (vis_lo >= kv0 + kb * 32 + 31) weights(std::false_type{});
+      if (dq_half_tile_unmasked(CAUSAL, wq0, kv0 + kb * 32, seq_len)) weights(std::false_type{});
       else weights(std::true_type{});
       // dQ^T += K^T dS^T, 16 keys at a time
 #pragma unroll
@@ -414,7 +413,7 @@ bwd_dkdv_kernel(BwdArgs a) {
         }
       };
       // the mask only where the half's queries meet the diagonal or a tail
-      if ((!CAUSAL || q0 + qb * 32 >= wk0 + 31) && q0 + qb * 32 + 32 <= seq_len && wk0 + 32 <= seq_len)
+      if (dkdv_half_tile_unmasked(CAUSAL, q0 + qb * 32, wk0, seq_len))
         weights(std::false_type{});
       else
         weights(std::true_type{});
@@ -604,7 +603,7 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
         }
       };
       // the mask only where this wave's queries meet the diagonal or a tail
-      if ((!CAUSAL || q0 + half * 32 >= wk0 + 31) && q0 + half * 32 + 32 <= seq_len && wk0 + 32 <= seq_len)
+      if (dkdv_half_tile_unmasked(CAUSAL, q0 + half * 32, wk0, seq_len))
         weights(std::false_type{});
       else
         weights(std::true_type{});

@@ -50,10 +50,9 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
   mx.dequantize_mx_*           pinned: exact on e4m3-grid values, error bound
 """
 from .exact import (attention, attention_rows, online_softmax_states,
-                        e4m3_decode, bf16_decode, dequantize_e4m3_blocks,
-                        visible_keys)
+                        e4m3_decode, bf16_decode, dequantize_e4m3_blocks)
 from . import backward, mx, quantize, rotation
 
 __all__ = ["attention", "attention_rows", "online_softmax_states",
-           "e4m3_decode", "bf16_decode", "dequantize_e4m3_blocks", "visible_keys",
+           "e4m3_decode", "bf16_decode", "dequantize_e4m3_blocks",
            "backward", "mx", "quantize", "rotation"]

@@ -39,11 +39,6 @@ import numpy as np
 _ROW_CHUNK = 512   # rows of scores held at once; bounds memory only
 
 
-def visible_keys(i: int, n: int, causal: bool) -> np.ndarray:
-    """Indices of the keys query i may see in a sequence of n tokens."""
-    return np.arange(i + 1 if causal else n)
-
-
 def _rows_plain(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                 row_ids: np.ndarray, causal: bool):
     """Exact attention for the query rows ``q_rows`` (positions ``row_ids``)
