@@ -702,7 +702,9 @@ def main():
     peak = PEAK[dtype]
     counters = counters_from_profiles(w.name)
     traffic = counters.get("bytes_per_launch")
-    clk = counters.get("clock_ghz")
+    # this run's own shader clock: the median of the power pass's sclk samples,
+    # taken during back-to-back launches of the same kernel
+    clk = power["sclk_mhz_median"] / 1000.0 if power and power.get("sclk_mhz_median") else None
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -726,6 +728,7 @@ def main():
                      "algorithmic_bytes": algorithmic_bytes(w),
                      # the published peak assumes 2.4 GHz; under this load the
                      # shader clock runs lower, which caps the attainable rate
+                     # (clock: this run's power pass, below)
                      "clock_ghz_measured": clk,
                      "peak_at_measured_clock": round(peak * clk / 2.4, 1) if clk else None,
                      "frac_at_measured_clock": round(tflops / (peak * clk / 2.4), 4) if clk else None},

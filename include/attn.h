@@ -52,6 +52,14 @@
  *   attn_fwd_mxfp8: MXFP8 q/k/v, o bf16, d = 128, fixed length or packed documents.
  *   attn_bwd:     bf16 gradients of attn_fwd (bf16 output), d in {64, 128}.
  *   Anything else returns an error; there is no fallback path.
+ *   Range: the forward kernels weigh keys against a reference maximum that
+ *   moves only when a tile's weights for a query sum past 2^64, so the
+ *   running sums l and u stay finite while N * max|v| < 2^68 (N the sequence
+ *   or document length, v the dequantised values).  Beyond that O may
+ *   overflow to inf or NaN although the exact result is finite.
+ *   fp8 / MXFP8 scores: dequantised Q and K values must be 0 or lie within
+ *   bf16's normal range (2^-126 <= |x| < 2^128); the scores are formed from
+ *   them as bf16 numbers.
  *
  * Ownership and concurrency
  *   Every pointer is device memory owned by the caller (except that `stream`
@@ -135,14 +143,18 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  *               attn_quantize_fp8 writes both layouts.
  *   o           bf16 [B][N][H][128] (packed [N][H][128]);  lse fp32 [B][H][N]
  *               (packed [H][N]).
- *   The probabilities P enter the P.V contraction as e4m3 as well, with one
- *   power-of-two scale 2^E per query row and 64-key tile, E the smallest
- *   integer with the row's weights in that tile summing to less than 2^E
- *   (weights of masked keys are 0, so a scale never depends on keys the row
- *   may not see).  P is carried as two e4m3 terms, P ~ hi + lo with
- *   hi = e4m3(P * 2^(8-E)) * 2^(E-8) and lo = e4m3((P - hi) * 2^(12-E)) *
- *   2^(E-12), each rounded to nearest: about 8 significant bits, as bf16.
- *   The normaliser l is summed from the unquantised fp32 P.  Scales must be
+ *   The scores are formed on the bf16 matrix instruction from the e4m3
+ *   values converted to bf16 (exact), with fp32 accumulation; the fp8 matrix
+ *   instruction truncates its partial sums too coarsely for them (see
+ *   attn_fwd_fp8.hip).  The probabilities P enter the P.V contraction as
+ *   e4m3, on the fp8 matrix instruction, with one power-of-two scale 2^E per
+ *   query row and 64-key tile, E the smallest integer with the row's weights
+ *   in that tile summing to less than 2^E (weights of masked keys are 0, so a
+ *   scale never depends on keys the row may not see).  P is carried as two
+ *   e4m3 terms, P ~ hi + lo with hi = e4m3(P * 2^(8-E)) * 2^(E-8) and
+ *   lo = e4m3((P - hi) * 2^(13-E)) * 2^(E-13), each rounded to nearest:
+ *   about 8 significant bits, as bf16.  The normaliser l is summed from the
+ *   unquantised fp32 P.  Scales must be
  *   positive, finite and normal.
  *   Other arguments as attn_fwd.  H * d must not exceed 2^24 (ATTN_ERR_SHAPE).
  */

@@ -12,15 +12,15 @@ from
   * D = rowsum(dO * O) is taken from the forward's bf16 O, so
     |D~ - D| <= sum_d |dO| |O~ - O| with O~ the HIP output;
   * dS = P (dP - D) is rounded to bf16 (2^-9 |dS|) before dQ and dK;
-  * the fp32 sums of d products behind S, dP and D, each within 2^-18 of its
-    sum of absolute products (the worst case of a 128-term fp32 sum is
-    2^-17; its typical error is 2^-20): this is what is left of dP - D when
+  * the fp32 sums of d products behind S, dP and D, each within 2^-17 of its
+    sum of absolute products (the worst case of a 128-term fp32 sum: 127
+    roundings of at most 2^-24 each): this is what is left of dP - D when
     one key holds all the weight and the two nearly cancel, and it moves P
-    by a relative |scale| 2^-18 (|q_i| . |k_j| + max_j' |q_i| . |k_j'|);
+    by a relative |scale| 2^-17 (|q_i| . |k_j| + max_j' |q_i| . |k_j'|);
   * the bf16 output rounding, half an ulp of the result.
 Propagated without cancellation, element by element:
     |dV~ - dV| <= (2^-7 + e_S) (P^T |dO|)                + half ulp
-    E = (2^-7 + e_S) P |dP - D| + P (|D~ - D| + 2^-18 (|dO| |V|^T + |dO| . |O|)) + 2^-9 |dS|
+    E = (2^-7 + e_S) P |dP - D| + P (|D~ - D| + 2^-17 (|dO| |V|^T + |dO| . |O|)) + 2^-9 |dS|
     |dQ~ - dQ| <= |scale| E |K|,  |dK~ - dK| <= |scale| E^T |Q|  (+ half ulp)
 That is a worst case (all errors of one sign); the Frobenius error of each
 gradient relative to its norm must also stay below 2^-7, which a
@@ -38,7 +38,7 @@ pytestmark = pytest.mark.gpu
 
 REL_P = 2.0 ** -7
 REL_DS = 2.0 ** -9
-REL_SUM = 2.0 ** -18
+REL_SUM = 2.0 ** -17
 ABS_FLOOR = 1e-5
 
 

@@ -143,6 +143,42 @@ def test_rising_scores(per_tile, N, d, causal):
         _check(q, k, v, scale, causal, out)
 
 
+@pytest.mark.parametrize("causal", [0, 1])
+def test_large_values_scale_exactly(causal):
+    """Inside the stated range (N * max|v| < 2^68) the result is exact up to
+    rounding at any magnitude of V: V times 2^48 gives O times 2^48, bit for
+    bit (fp32 output; every product and partial sum just moves up 48
+    binades), and the same LSE."""
+    q, k, v = _case(81, (1, 2048, 2, 128), outliers="qk")
+    O1, L1, _ = run_bf16(q, k, v, 1 / math.sqrt(128), causal, out="f32")
+    v48 = W.f32_to_bf16_bits(W.bf16_bits_to_f32(v) * np.float32(2.0 ** 48))
+    O2, L2, _ = run_bf16(q, k, v48, 1 / math.sqrt(128), causal, out="f32")
+    assert np.all(np.isfinite(O2))
+    assert np.array_equal(O2, O1 * 2.0 ** 48) and np.array_equal(L1, L2)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_large_weights_and_values(causal):
+    """Scores rising by about 50 exp2 units per 64-key tile keep weights of up
+    to ~2^50 against the lazy reference, with V scaled by 2^40: still inside
+    the range, and within the fp32-output tolerance relative to 2^40."""
+    d, N = 128, 640
+    scale = 1 / math.sqrt(d)
+    c = scale / math.log(2.0)
+    slope = 50.0 / (64 * 4.0 * c)
+    rng = np.random.default_rng(82 + causal)
+    q = rng.standard_normal((1, N, 2, d)).astype(np.float32) * np.float32(0.05)
+    q[..., 0] = 4.0
+    k = rng.standard_normal((1, N, 2, d)).astype(np.float32)
+    k[..., 0] = (np.float32(slope) * np.arange(N, dtype=np.float32))[None, :, None]
+    v = rng.standard_normal((1, N, 2, d)).astype(np.float32) * np.float32(2.0 ** 40)
+    q, k, v = (W.f32_to_bf16_bits(x) for x in (q, k, v))
+    O, L, _ = run_bf16(q, k, v, scale, causal, out="f32")
+    Or, Lr = oracle_bf16(q, k, v, scale, causal)
+    err = errors(O / 2.0 ** 40, Or / 2.0 ** 40, L, Lr, out="f32")
+    assert_within(err, TOL_F32)
+
+
 def test_value_outliers_bound():
     """With +-20 outliers in V as well, the bf16 rounding of P before the P.V
     contraction bounds the error by u * max|v| (u = 2^-8, the unit roundoff
