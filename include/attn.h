@@ -65,7 +65,8 @@
  *   Every pointer is device memory owned by the caller (except that `stream`
  *   is a HIP stream handle, NULL for the null stream).  The library allocates
  *   nothing, keeps no pointer after returning, has no mutable global state
- *   and may be called from several threads at once.  Every pointer must be
+ *   (except the fixed scratch of attn_bwd_noalloc and its cached per-device
+ *   address) and may be called from several threads at once.  Every pointer must be
  *   16-byte aligned.  Inputs are never written; o and lse are fully
  *   overwritten.
  *
@@ -96,7 +97,8 @@ typedef enum {
     ATTN_ERR_UNSUPPORTED = 3,  /* d, dtype or causal flag not supported              */
     ATTN_ERR_SCALE = 4,        /* scale is NaN or infinite                           */
     ATTN_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned                   */
-    ATTN_ERR_HIP = 6           /* the kernel launch failed                           */
+    ATTN_ERR_HIP = 6,          /* the kernel launch failed                           */
+    ATTN_ERR_SCRATCH = 7       /* attn_bwd_noalloc: more rows than its fixed scratch */
 } attn_status;
 
 typedef enum {
@@ -192,6 +194,31 @@ ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, float* delta, void* dq, void* dk, void* dv,
                       int B, int H, int N, int d, float scale, int causal,
                       const int32_t* cu_seqlens, void* stream);
+
+/*
+ * attn_bwd_noalloc - attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, bit for bit, without the `delta`
+ * argument.  D per row goes to a fixed scratch array that the library keeps
+ * in each GPU's memory until the process ends (2^21 floats, 8 MiB per GPU);
+ * its device address is looked up once per device, on the first call made
+ * with that device current.  The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine) and reads nothing a previous call
+ * left in the scratch (D is written before it is read).
+ *   Arguments as attn_bwd, without delta.
+ *   Rows of D - B * H * N (fixed length) or H * N (packed) - must not exceed
+ *   2^21 (ATTN_ERR_SCRATCH otherwise; nothing is enqueued).
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *   on one GPU (different streams, or several threads) race and give
+ *   undefined results; serialise them, or use attn_bwd with a delta buffer
+ *   each.  The current device must be the one `stream` belongs to.
+ *   Errors as attn_bwd, plus ATTN_ERR_SCRATCH, and ATTN_ERR_HIP when the
+ *   scratch's address cannot be obtained.
+ */
+ATTN_API int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv,
+                              int B, int H, int N, int d, float scale, int causal,
+                              const int32_t* cu_seqlens, void* stream);
 
 /*
  * attn_fwd_mxfp8 - exact attention forward on MXFP8 operands (d = 128), the

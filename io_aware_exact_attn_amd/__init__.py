@@ -17,13 +17,13 @@ import os
 
 __all__ = [
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_SCALE",
-    "ATTN_ERR_ALIGN", "ATTN_ERR_HIP", "ATTN_BF16", "ATTN_BF16_OUT_F32", "ATTN_FP8_E4M3",
-    "AttnError", "attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_quantize_fp8", "attn_status_str", "attn_kernel_name",
+    "ATTN_ERR_ALIGN", "ATTN_ERR_HIP", "ATTN_ERR_SCRATCH", "ATTN_BF16", "ATTN_BF16_OUT_F32", "ATTN_FP8_E4M3",
+    "AttnError", "attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_noalloc", "attn_quantize_fp8", "attn_status_str", "attn_kernel_name",
     "library_path", "lib",
 ]
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED = 0, 1, 2, 3
-ATTN_ERR_SCALE, ATTN_ERR_ALIGN, ATTN_ERR_HIP = 4, 5, 6
+ATTN_ERR_SCALE, ATTN_ERR_ALIGN, ATTN_ERR_HIP, ATTN_ERR_SCRATCH = 4, 5, 6, 7
 ATTN_BF16, ATTN_BF16_OUT_F32, ATTN_FP8_E4M3 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,6 +51,8 @@ lib.attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
 lib.attn_fwd_fp8.restype = _i
 lib.attn_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _vp, _vp]
 lib.attn_bwd.restype = _i
+lib.attn_bwd_noalloc.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _vp, _vp]
+lib.attn_bwd_noalloc.restype = _i
 lib.attn_quantize_fp8.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
 lib.attn_quantize_fp8.restype = _i
 lib.attn_quantize_fp8_rotated.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
@@ -176,4 +178,17 @@ def attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale, causal
                       _ptr(cu_seqlens), _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
+    return st
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens=None,
+                     stream=None, check: bool = True) -> int:
+    """Enqueue the bf16 attention backward without a caller workspace (see
+    ``attn_bwd_noalloc`` in include/attn.h): D goes to the library's fixed
+    per-GPU scratch."""
+    st = lib.attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), int(B), int(H), int(N), int(d), float(scale), int(causal),
+                              _ptr(cu_seqlens), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_noalloc")
     return st

@@ -1,5 +1,6 @@
 // C ABI of the attention library: argument validation (host only, before any
-// HIP call), kernel selection and launch.  No allocation, no global state.
+// HIP call), kernel selection and launch.  No allocation; the only global
+// state is the per-device address of attn_bwd_noalloc's fixed scratch.
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
@@ -38,6 +39,33 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
   a.c = (float)c;
   a.qsign = std::signbit(scale) ? 0x80008000u : 0u;
   a.lse_mul = 0.6931471805599453f;
+  return ATTN_OK;
+}
+
+// Checks shared by the two backward entry points (everything but the D
+// workspace); fills `a` except a.delta.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              const void* dq, const void* dk, const void* dv, int B, int H, int N, int d, float scale, int causal,
+              const int32_t* cu_seqlens, iaea::BwdArgs& a) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * N * H >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if ((int64_t)H * d > ((int64_t)1 << 24)) return ATTN_ERR_SHAPE;
+  for (const void* p : {q, k, v, o, dout, (const void*)lse, dq, dk, dv})
+    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+  if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
+  const int64_t bm = iaea::bwd_rows_per_workgroup();
+  if (cu_seqlens && (int64_t)H * ((N + bm - 1) / bm + B) + 8 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  a = iaea::BwdArgs{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = const_cast<void*>(dq); a.dk = const_cast<void*>(dk); a.dv = const_cast<void*>(dv);
+  a.cu_seqlens = cu_seqlens;
+  a.B = B; a.H = H; a.N = N;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
   return ATTN_OK;
 }
 
@@ -123,25 +151,29 @@ ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, float* delta, void* dq, void* dk, void* dv,
                       int B, int H, int N, int d, float scale, int causal,
                       const int32_t* cu_seqlens, void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return ATTN_ERR_NULL;
-  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
-  if ((int64_t)B * N * H >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
-  if ((int64_t)H * d > ((int64_t)1 << 24)) return ATTN_ERR_SHAPE;
-  for (const void* p : {q, k, v, o, dout, (const void*)lse, (const void*)delta, (const void*)dq,
-                        (const void*)dk, (const void*)dv})
-    if (!aligned16(p)) return ATTN_ERR_ALIGN;
-  if (cu_seqlens && !aligned16(cu_seqlens)) return ATTN_ERR_ALIGN;
-  const int64_t bm = iaea::bwd_rows_per_workgroup();
-  if (cu_seqlens && (int64_t)H * ((N + bm - 1) / bm + B) + 8 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-  iaea::BwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.delta = delta;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.cu_seqlens = cu_seqlens;
-  a.B = B; a.H = H; a.N = N;
-  a.scale = scale;
-  a.c = (float)((double)scale * 1.4426950408889634);
+  if (!delta) return ATTN_ERR_NULL;
+  iaea::BwdArgs a;
+  const int st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens, a);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(delta)) return ATTN_ERR_ALIGN;
+  a.delta = delta;
+  const hipError_t e = iaea::launch_attn_bwd(a, d, causal == 1, cu_seqlens != nullptr,
+                                             reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+ATTN_API int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv,
+                              int B, int H, int N, int d, float scale, int causal,
+                              const int32_t* cu_seqlens, void* stream) {
+  iaea::BwdArgs a;
+  const int st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens, a);
+  if (st != ATTN_OK) return st;
+  const int64_t rows = (int64_t)(cu_seqlens ? 1 : B) * N * H;
+  if (rows > iaea::kBwdScratchRows) return ATTN_ERR_SCRATCH;
+  float* scratch = nullptr;
+  if (iaea::bwd_scratch_address(&scratch) != hipSuccess) return ATTN_ERR_HIP;
+  a.delta = scratch;
   const hipError_t e = iaea::launch_attn_bwd(a, d, causal == 1, cu_seqlens != nullptr,
                                              reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -212,6 +244,7 @@ ATTN_API const char* attn_status_str(int status) {
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_HIP: return "kernel launch failed";
+    case ATTN_ERR_SCRATCH: return "more rows than the fixed scratch of attn_bwd_noalloc holds (2^21)";
     default: return "unknown status";
   }
 }

@@ -30,6 +30,8 @@
 // (buffer_load_dwordx4 ... lds); P and dS are rounded to bf16 and reused as
 // the B operand of the next product in the accumulator's own register order,
 // with the A operand read in the matching order by ds_read_b64_tr_b16.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -709,5 +711,42 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int d, bool causal, bool packed, hi
 }
 
 int bwd_rows_per_workgroup() { return bwd::BM; }
+
+// ---------------------------------------------------------------------------
+// fixed scratch of the no-allocation entry point
+// ---------------------------------------------------------------------------
+
+// D per row for callers that cannot allocate: a file-scope device array, one
+// copy per GPU, alive until the process ends.  In host code the name is only a
+// stand-in for the symbol; kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) float scratch[kBwdScratchRows];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t bwd_scratch_address(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      p = static_cast<float*>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 }  // namespace iaea

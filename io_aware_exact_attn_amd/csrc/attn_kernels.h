@@ -21,6 +21,13 @@ hipError_t launch_attn_fwd_mxfp8(const FwdArgs& a, bool causal, bool packed, hip
 hipError_t launch_attn_bwd(const BwdArgs& a, int d, bool causal, bool packed, hipStream_t st);
 int bwd_rows_per_workgroup();
 
+// Rows of D (B * H * N, or H * N packed) that the fixed scratch of the
+// no-allocation backward holds: 2^21 floats, 8 MiB per GPU.
+constexpr int64_t kBwdScratchRows = (int64_t)1 << 21;
+// Device address of that scratch on the current device (looked up once per
+// device, then cached).
+hipError_t bwd_scratch_address(float** out);
+
 // bf16 -> e4m3 with per-128-token block scales; d in {64, 128}.
 hipError_t launch_quantize_fp8(const QuantArgs& a, int d, bool packed, hipStream_t st);
 hipError_t launch_quantize_fp8_rotated(const QuantArgs& a, int d, bool packed, hipStream_t st);

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_quantize_fp8_rotated", "attn_quantize_mxfp8", "attn_fwd_mxfp8", "attn_bwd",
-                                         "attn_status_str", "attn_kernel_name"}
+                                         "attn_bwd_noalloc", "attn_status_str", "attn_kernel_name"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -187,8 +187,28 @@ def test_attn_bwd_rejects(kw, status):
     assert bwd(**kw) == status
 
 
+def bwd_noalloc(**kw):
+    args = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, H=2, N=300, d=128,
+                scale=0.1, causal=1, cu_seqlens=None, stream=0)
+    args.update(kw)
+    return ia.attn_bwd_noalloc(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ia.ATTN_ERR_NULL), (dict(lse=None), ia.ATTN_ERR_NULL), (dict(dk=None), ia.ATTN_ERR_NULL),
+    (dict(B=0), ia.ATTN_ERR_SHAPE), (dict(d=96), ia.ATTN_ERR_UNSUPPORTED), (dict(causal=5), ia.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=float("inf")), ia.ATTN_ERR_SCALE), (dict(dv=MIS), ia.ATTN_ERR_ALIGN),
+    (dict(cu_seqlens=MIS), ia.ATTN_ERR_ALIGN),
+    # D rows beyond the fixed 2^21-row scratch: fixed length B * H * N, packed H * N
+    (dict(B=2, H=16, N=(1 << 16) + 1), ia.ATTN_ERR_SCRATCH),
+    (dict(cu_seqlens=P, B=3, H=32, N=(1 << 16) + 1), ia.ATTN_ERR_SCRATCH),
+])
+def test_attn_bwd_noalloc_rejects(kw, status):
+    assert bwd_noalloc(**kw) == status
+
+
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert ia.attn_status_str(s) and ia.attn_status_str(s) != "unknown status"
     assert ia.attn_status_str(99) == "unknown status"
     assert ia.attn_status_str(-1) == "unknown status"
