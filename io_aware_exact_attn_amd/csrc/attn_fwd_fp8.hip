@@ -77,7 +77,9 @@ __device__ __forceinline__ int lds_off(int row, int granule) {
   return row * ROWB + ((granule ^ swz(row)) << 4);
 }
 
-__device__ __forceinline__ i32x2 ds_read_tr8(const char* p) {
+// The restrict-qualified pointer gives the read alias-scope metadata, so the
+// compiler does not wait for the next tile's in-flight LDS DMA before it.
+__device__ __forceinline__ i32x2 ds_read_tr8(const char* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((IAEA_LDS i32x2*)(p));
 }
 

@@ -191,13 +191,12 @@ def test_bwd_gradient_outliers():
     check_case((q, k, v, do), 1.0 / np.sqrt(128), True)
 
 
-def test_bwd_long_context_sampled():
+@pytest.fixture(scope="module")
+def long_context_run():
     """The long-context causal workload (B 1, H 32, N 16384, d 128) with the
-    seeded dO and the single attn_bwd launch sequence that `bench.py --extra
-    bwd` times; dQ rows and dK/dV rows sampled in two heads (first and last
-    rows, tile and block edges) against the row-sampled oracle, each element
-    within the bound of this file's docstring (the max over keys of
-    |q_i| . |k_j| there bounded by sum_d |q_id| max_j |k_jd|)."""
+    seeded dO, run once through the forward and the single attn_bwd launch
+    sequence that `bench.py --extra bwd` times; returns the inputs and the
+    outputs on the host."""
     import torch
     import io_aware_exact_attn_amd as ia
     w = W.workload(3)
@@ -213,60 +212,87 @@ def test_bwd_long_context_sampled():
     g = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
     ia.attn_bwd(dev[0], dev[1], dev[2], o, dev[3], lse, delta, g[0], g[1], g[2], B, H, N, d, w.scale, 1, None)
     torch.cuda.synchronize()
+    host = lambda t: t.float().cpu().numpy()
+    return w, inp, do_bits, host(o), [host(t) for t in g], host(delta)
+
+
+def _long_context_head(run, h, rows):
+    w, inp, do_bits, o, g, delta = run
+    qh, kh, vh, doh = (oracle.bf16_decode(x[0, :, h]) for x in (inp["q"], inp["k"], inp["v"], do_bits))
+    f64 = lambda x: x.astype(np.float64)
+    _check_sampled_rows(qh, kh, vh, doh, f64(o[0, :, h]), [f64(t[0, rows, h]) for t in g],
+                        f64(delta[0, h, rows]), rows, w.scale)
+
+
+def test_bwd_long_context_sampled(long_context_run):
+    """Long-context workload: dQ rows and dK/dV rows sampled in two heads
+    (first and last rows, tile and block edges) against the row-sampled
+    oracle, each element within the bound of this file's docstring."""
     rows = np.array([0, 1, 63, 64, 127, 128, 129, 4095, 8191, 12000, 16382, 16383])
-    for h in (0, 21):
-        qh, kh, vh, doh = (oracle.bf16_decode(x[0, :, h]) for x in (inp["q"], inp["k"], inp["v"], do_bits))
-        _check_sampled_rows(qh, kh, vh, doh, o[0, :, h].float().cpu().numpy().astype(np.float64),
-                            [t[0, rows, h].float().cpu().numpy().astype(np.float64) for t in g],
-                            delta[0, h, rows].cpu().numpy().astype(np.float64), rows, w.scale)
+    for h in (7, 30):
+        _long_context_head(long_context_run, h, rows)
 
 
-def _check_sampled_rows(qh, kh, vh, doh, o_gpu, got, dl, rows, sc):
+@pytest.mark.parametrize("h", [0, 21])
+def test_bwd_long_context_all_rows(long_context_run, h):
+    """Long-context workload: every row of dQ, dK and dV of head h against
+    the oracle, each element within the bound of this file's docstring."""
+    _long_context_head(long_context_run, h, np.arange(long_context_run[0].N))
+
+
+def _check_sampled_rows(qh, kh, vh, doh, o_gpu, got, dl, rows, sc, chunk=2048):
     """dQ rows and dK/dV rows of one causal (sequence, head) at `rows`
     against the row-sampled oracle, each element within the bound of this
     file's docstring (the max over keys of |q_i| . |k_j| there bounded by
-    sum_d |q_id| max_j |k_jd|); `dl` is the kernel's D at those rows."""
+    sum_d |q_id| max_j |k_jd|); `dl` is the kernel's D at those rows.  The
+    bounds are formed `chunk` rows at a time, so every row of a long
+    sequence can be checked without an n x n matrix per term."""
     N = qh.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
     dq, dk, dv, parts = ob.grads_at(qh, kh, vh, doh, sc, True, rows, rows)
     L, D, O = parts["L"], parts["D"], parts["O"]
     err_d = (np.abs(doh) * np.abs(o_gpu - O)).sum(axis=1)
     qk_max = np.abs(qh) @ np.abs(kh).max(axis=0)
     sums_row = REL_SUM * (np.abs(doh) * np.abs(O)).sum(axis=1)
-
-    # dQ rows: all keys
-    s = sc * (qh[rows] @ kh.T)
-    s = np.where(np.arange(N)[None, :] > rows[:, None], -np.inf, s)
-    p = np.exp(s - L[rows][:, None])
-    dp = doh[rows] @ vh.T
-    rel = REL_P + abs(sc) * REL_SUM * (np.abs(qh[rows]) @ np.abs(kh).T + qk_max[rows][:, None])
-    sums = REL_SUM * (np.abs(doh[rows]) @ np.abs(vh).T) + sums_row[rows][:, None]
-    e = rel * p * np.abs(dp - D[rows][:, None]) + p * (err_d[rows][:, None] + sums) + \
-        REL_DS * np.abs(p * (dp - D[rows][:, None]))
-    bq = abs(sc) * (e @ np.abs(kh))
-    # dK, dV rows: all queries
-    s = sc * (qh @ kh[rows].T)
-    s = np.where(rows[None, :] > np.arange(N)[:, None], -np.inf, s)
-    p = np.exp(s - L[:, None])
-    dp = doh @ vh[rows].T
-    rel = REL_P + abs(sc) * REL_SUM * (np.abs(qh) @ np.abs(kh[rows]).T + qk_max[:, None])
-    sums = REL_SUM * (np.abs(doh) @ np.abs(vh[rows]).T) + sums_row[:, None]
-    e = rel * p * np.abs(dp - D[:, None]) + p * (err_d[:, None] + sums) + REL_DS * np.abs(p * (dp - D[:, None]))
-    bk = abs(sc) * (e.T @ np.abs(qh))
-    bv = (rel * p).T @ np.abs(doh)
-    for name, gg, ref, bnd in zip(("dq", "dk", "dv"), got, (dq, dk, dv), (bq, bk, bv)):
-        lim = bnd + bf16_half_ulp(np.maximum(np.abs(gg), np.abs(ref))) + ABS_FLOOR
-        ratio = float((np.abs(gg - ref) / lim).max())
-        assert np.all(np.isfinite(gg)) and ratio <= 1.0, (name, ratio)
+    aq, ak, av, ado = np.abs(qh), np.abs(kh), np.abs(vh), np.abs(doh)
+    for c0 in range(0, len(rows), chunk):
+        r = rows[c0:c0 + chunk]
+        sl = slice(c0, c0 + len(r))
+        # dQ rows: all keys
+        s = sc * (qh[r] @ kh.T)
+        s = np.where(np.arange(N)[None, :] > r[:, None], -np.inf, s)
+        p = np.exp(s - L[r][:, None])
+        dpd = doh[r] @ vh.T - D[r][:, None]
+        rel = REL_P + abs(sc) * REL_SUM * (aq[r] @ ak.T + qk_max[r][:, None])
+        sums = REL_SUM * (ado[r] @ av.T) + sums_row[r][:, None]
+        e = rel * p * np.abs(dpd) + p * (err_d[r][:, None] + sums) + REL_DS * np.abs(p * dpd)
+        bq = abs(sc) * (e @ ak)
+        # dK, dV rows: all queries
+        s = sc * (qh @ kh[r].T)
+        s = np.where(r[None, :] > np.arange(N)[:, None], -np.inf, s)
+        p = np.exp(s - L[:, None])
+        dpd = doh @ vh[r].T - D[:, None]
+        rel = REL_P + abs(sc) * REL_SUM * (aq @ ak[r].T + qk_max[:, None])
+        sums = REL_SUM * (ado @ av[r].T) + sums_row[:, None]
+        e = rel * p * np.abs(dpd) + p * (err_d[:, None] + sums) + REL_DS * np.abs(p * dpd)
+        bk = abs(sc) * (e.T @ aq)
+        bv = (rel * p).T @ ado
+        for name, gg, ref, bnd in zip(("dq", "dk", "dv"), got, (dq, dk, dv), (bq, bk, bv)):
+            gg, ref = gg[sl], ref[sl]
+            lim = bnd + bf16_half_ulp(np.maximum(np.abs(gg), np.abs(ref))) + ABS_FLOOR
+            ratio = float((np.abs(gg - ref) / lim).max())
+            assert np.all(np.isfinite(gg)) and ratio <= 1.0, (name, int(r[0]), ratio)
     assert np.all(np.abs(dl - (o_gpu[rows] * doh[rows]).sum(axis=1)) <= 1e-5 * (np.abs(o_gpu[rows]) *
                                                                                 np.abs(doh[rows])).sum(axis=1))
 
 
 @pytest.mark.parametrize("cid", [2, 4])
-def test_bwd_workload_sampled(cid):
+def test_bwd_workload_rows(cid):
     """The multi-head causal (B 4, H 16, N 2048, d 128) and packed-document
     (26 documents, 32768 tokens, H 16, d 128) workloads with the seeded dO and
-    the launch sequence that `bench.py --extra bwd` times; rows sampled (first
-    and last, tile edges, middle) in two (sequence or document, head) pairs."""
+    the launch sequence that `bench.py --extra bwd` times; every row of dQ, dK
+    and dV in two (sequence or document, head) pairs (the longest document
+    and a median one when packed)."""
     import torch
     import io_aware_exact_attn_amd as ia
     w = W.workload(cid)
@@ -300,12 +326,12 @@ def test_bwd_workload_sampled(cid):
             a, b = seq
             n = b - a
             take = [x[a:b, h] for x in (inp["q"], inp["k"], inp["v"], do_bits)]
-            rows = np.unique(np.clip([0, 1, 63, 64, 127, 128, n // 2, n - 2, n - 1], 0, n - 1))
+            rows = np.arange(n)
             o_h, got = f64(o[a:b, h]), [f64(t[a + rows, h]) for t in g]
             dl = f64(delta[h, a + rows])
         else:
             take = [x[seq, :, h] for x in (inp["q"], inp["k"], inp["v"], do_bits)]
-            rows = np.array([0, 1, 63, 64, 127, 128, 129, 1023, 2046, 2047])
+            rows = np.arange(w.N)
             o_h, got = f64(o[seq, :, h]), [f64(t[seq, rows, h]) for t in g]
             dl = f64(delta[seq, h, rows])
         qh, kh, vh, doh = (oracle.bf16_decode(x) for x in take)
