@@ -208,6 +208,26 @@ def cpu_baseline(w, inp, O_gpu, budget_s):
             "seconds": round(dt, 3), "max_abs_err_vs_gpu_on_sample": max_err}
 
 
+def _time_cold(fn, reps=5, flush_mib=512):
+    """Median time (ms) of fn() when its inputs are not cached: a scratch
+    write of flush_mib MiB before each call evicts L2 and the Infinity Cache;
+    HIP events bracket the call only."""
+    import torch
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    per = []
+    for i in range(reps):
+        scratch.fill_(float(i))
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        fn()
+        b_.record(stream)
+        b_.synchronize()
+        per.append(a_.elapsed_time(b_))
+    del scratch
+    return float(np.median(per))
+
+
 def _time_launches(fn, steps, warmup):
     """Median and mean per-call time (ms) of fn() on the current stream, HIP
     events around each call, after warmup calls."""
@@ -276,12 +296,16 @@ def extra_quantize(args):
             for x, y, sc in zip(xs, ys, ss):
                 ia.attn_quantize_fp8(x, y, sc, B, w.H, N, w.d, cu)
         med, mean = _time_launches(step, args.steps, args.warmup)
+        cold = _time_cold(lambda: ia.attn_quantize_fp8(xs[0], ys[0], ss[0], B, w.H, N, w.d, cu))
         elems = int(np.prod(shape))
         per_launch_bytes = elems * 3 + nblocks * 4
         t_launch = mean / 3           # back-to-back launches, as the headline line times them
         out[name] = {"shape": list(shape), "per_step_ms_median": round(med, 5), "per_step_ms_mean": round(mean, 5),
                      "algorithmic_bytes_per_launch": per_launch_bytes,
-                     "gbps": round(per_launch_bytes / (t_launch * 1e-3) / 1e9, 1)}
+                     "gbps": round(per_launch_bytes / (t_launch * 1e-3) / 1e9, 1),
+                     # one launch with L2 and the Infinity Cache evicted first
+                     "cold_ms_per_launch": round(cold, 5),
+                     "cold_gbps": round(per_launch_bytes / (cold * 1e-3) / 1e9, 1)}
     f = out["fixed"]
     res["value"] = f["gbps"]
     res["config"] = {"workload": "quantise q, k, v of fp8_block_scaled_causal_b2_h16_n8192_d128 "
@@ -384,6 +408,8 @@ def extra_mxfp8(args):
         ia.attn_quantize_mxfp8(xs[2], ys[2], ss[2], B, H, N, d, None, 1)
     qd_med, qd_mean = _time_launches(quant_d, args.steps, args.warmup)
     qt_med, qt_mean = _time_launches(quant_t, args.steps, args.warmup)
+    qd_cold = _time_cold(quant_d)
+    qt_cold = _time_cold(quant_t)
     o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
 
@@ -405,7 +431,13 @@ def extra_mxfp8(args):
                       "quantise_qk_along_d_ms": round(qd_mean, 5),
                       "quantise_qk_along_d_gbps": round(2 * qbytes / (qd_mean * 1e-3) / 1e9, 1),
                       "quantise_v_along_tokens_ms": round(qt_mean, 5),
-                      "quantise_v_along_tokens_gbps": round(qbytes / (qt_mean * 1e-3) / 1e9, 1)},
+                      "quantise_v_along_tokens_gbps": round(qbytes / (qt_mean * 1e-3) / 1e9, 1),
+                      # back to back the 67 MB inputs stay in the 256 MB Infinity Cache; the
+                      # cache-cold figures evict it before each call
+                      "quantise_qk_along_d_cold_ms": round(qd_cold, 5),
+                      "quantise_qk_along_d_cold_gbps": round(2 * qbytes / (qd_cold * 1e-3) / 1e9, 1),
+                      "quantise_v_along_tokens_cold_ms": round(qt_cold, 5),
+                      "quantise_v_along_tokens_cold_gbps": round(qbytes / (qt_cold * 1e-3) / 1e9, 1)},
            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK["fp8"], "unit": "TFLOP/s",
                         "frac": round(tf / PEAK["fp8"], 4), "traffic": None}}
     if not args.no_cpu_baseline:
