@@ -310,7 +310,9 @@ def extra_quantize(args):
     res["value"] = f["gbps"]
     res["config"] = {"workload": "quantise q, k, v of fp8_block_scaled_causal_b2_h16_n8192_d128 "
                                  "(one step = 3 launches)",
-                     "kernel": "quantize_fp8_kernel<128,fixed>", "packed": out["packed"]}
+                     "kernel": "quantize_fp8_kernel<128,fixed>",
+                     "cold_ms_per_launch": f["cold_ms_per_launch"], "cold_gbps": f["cold_gbps"],
+                     "packed": out["packed"]}
     res["ms_per_step"] = f["per_step_ms_mean"]
     res["roofline"] = {"bound": "hbm", "achieved": f["gbps"], "peak": HBM_PEAK, "unit": "GB/s",
                        "frac": round(f["gbps"] / HBM_PEAK, 4), "traffic": None}

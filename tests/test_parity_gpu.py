@@ -194,6 +194,40 @@ def test_value_outliers_bound():
 # the five workloads (bf16 ones here)
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_max_head_stride(d, causal):
+    """H * d at the boundary's 2^24 limit (H = 2^24 / d heads): one 64-token
+    tile of all heads spans 2^31 bytes, the most the kernels' 32-bit tile
+    offsets and buffer sizes allow.  N = 65 gives a full tile and a one-row
+    tail.  Four heads (first, second, middle, last) hold seeded inputs, the
+    rest zeros; those four are compared with the oracle."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    B, N = 1, 65
+    H = (1 << 24) // d
+    heads = [0, 1, H // 2, H - 1]
+    scale = 1.0 / math.sqrt(d)
+    bits = {t: W.normal_bf16(9100 + 10 * d + i, (B, N, len(heads), d)) for i, t in enumerate("qkv")}
+    dev = {}
+    for t in "qkv":
+        x = torch.zeros((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+        for j, h in enumerate(heads):
+            x[:, :, h] = torch.from_numpy(np.ascontiguousarray(bits[t][:, :, j]).view(np.int16)).view(
+                torch.bfloat16).cuda()
+        dev[t] = x
+    o = torch.full((B, N, H, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ia.attn_fwd(dev["q"], dev["k"], dev["v"], o, lse, B, H, N, d, scale, causal, None, ia.ATTN_BF16)
+    torch.cuda.synchronize()
+    O = o[:, :, heads].float().cpu().numpy().astype(np.float64)
+    L = lse[:, heads].cpu().numpy().astype(np.float64)
+    del dev, o, lse
+    torch.cuda.empty_cache()
+    Or, Lr = oracle_bf16(bits["q"], bits["k"], bits["v"], scale, causal)
+    assert_within(errors(O, Or, L, Lr, out="bf16"), TOL_BF16)
+
+
 def test_workload1_single_head():
     w = W.workload(1)
     inp = W.make_inputs(w)
