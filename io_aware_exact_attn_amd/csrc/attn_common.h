@@ -164,22 +164,28 @@ __device__ __forceinline__ bool decode_work(const Args& a, int bid, int& h, int&
       // The last workgroups to start are those of the shortest documents.
       const int t = bid / a.H;
       h = bid - t * a.H;
-      const int len = lane < a.B ? a.cu_seqlens[lane + 1] - a.cu_seqlens[lane] : 0;
+      // lane f holds document f's start and length: one load of each bound,
+      // and the start comes back from its lane instead of a second load
+      // (lanes past the last document read the last bound twice: length 0;
+      // the loads and the loop below are branch-free)
+      const int c0 = a.cu_seqlens[min(lane, a.B)];
+      const int len = a.cu_seqlens[min(lane + 1, a.B)] - c0;
       const int nb = len > 0 ? (len + BM - 1) / BM : 0;
-      int rank = 0;                            // documents before this one in the order
+      // items before this document's first: the work of every document that
+      // comes before it in the order (longer, or as long and earlier)
+      int first = 0;
       for (int f = 0; f < a.B; ++f) {
         const int lf = __builtin_amdgcn_readlane(len, f);
-        rank += (lf > len) || (lf == len && f < lane);
+        const int nf = __builtin_amdgcn_readlane(nb, f);
+        const int before = (int)(lf > len) | ((int)(lf == len) & (int)(f < lane));
+        first += nf & -before;
       }
-      int first = 0;                           // items before this document's first
-      for (int f = 0; f < a.B; ++f)
-        first += (__builtin_amdgcn_readlane(rank, f) < rank) ? __builtin_amdgcn_readlane(nb, f) : 0;
       const unsigned long long m = __ballot(lane < a.B && t >= first && t < first + nb);
       if (m == 0) return false;
       const int doc = __ffsll((long long)m) - 1;
       const int r = t - __builtin_amdgcn_readlane(first, doc);
       const int nbd = __builtin_amdgcn_readlane(nb, doc);
-      seq_start = a.cu_seqlens[doc];
+      seq_start = __builtin_amdgcn_readlane(c0, doc);
       seq_len = __builtin_amdgcn_readlane(len, doc);
       qblk = CAUSAL ? (nbd - 1 - r) : r;
       b = doc;
