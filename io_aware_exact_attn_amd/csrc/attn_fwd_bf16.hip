@@ -299,9 +299,12 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           for (int r = 0; r < 16; ++r)
             if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) sc[kb][r] = -INFINITY;
       }
-      float lx = weights(0.f, false);
+      // a row's first tile (the same tile for every lane of the wave) goes
+      // straight to the maximum; later tiles form their weights first
       const bool first = m_run == -INFINITY;
-      if (__ballot(lx > kLazyMax || first) != 0) {
+      float lx = 0.f;
+      if (!first) lx = weights(0.f, false);
+      if (__ballot(first || lx > kLazyMax) != 0) {
         float m = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
         for (int r = 1; r < 16; ++r) m = fmaxf(m, fmaxf(sc[0][r], sc[1][r]));

@@ -338,12 +338,15 @@ attn_fwd_fp8_kernel(FwdArgs a) {
         return xb[0] + xb[1];
       };
       scores();
-      float lx = weights();
+      // a row's first tile (the same tile for every lane of the wave) takes
+      // its maximum before the weights; later tiles form their weights first
       const bool first = m_run == -INFINITY;
-      if (__ballot(lx > kLazyMax || first) != 0) {
-        // rare: the reference moves to the tile maximum (the scores are formed
-        // again, their registers now hold weights)
-        scores();
+      float lx = 0.f;
+      if (!first) lx = weights();
+      if (__ballot(first || lx > kLazyMax) != 0) {
+        // the reference moves to the tile maximum (rare after the first tile;
+        // then the scores are formed again, their registers hold weights)
+        if (!first) scores();
         float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
