@@ -576,14 +576,29 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
     const int q0 = j * BN;
     bf16x8 own_p[2], own_ds[2];
     if (live) {
-      // S and dP of this wave's 32 queries (rows 32 half .. of the tile)
+      // S and dP of this wave's 32 queries (rows 32 half .. of the tile): 16
+      // MFMA steps, S and dP alternating, each operand fragment read PF steps
+      // ahead of its MFMA so the LDS latency hides behind earlier MFMAs
       f32x16 s, dp;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 qfr = *(const bf16x8*)(qt + half * 32 * ROWB + qoff[dc]);
-        const bf16x8 dfr = *(const bf16x8*)(dt + half * 32 * ROWB + qoff[dc]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr, kf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
+      {
+        constexpr int PF = 3;
+        auto afrag = [&](auto step) __attribute__((always_inline)) -> bf16x8 {
+          constexpr int st = decltype(step)::value;
+          return *(const bf16x8*)(((st & 1) ? dt : qt) + half * 32 * ROWB + qoff[st >> 1]);
+        };
+        bf16x8 fa[PF + 1];
+        static_for<PF>([&](auto step) __attribute__((always_inline)) {
+          fa[decltype(step)::value] = afrag(step);
+        });
+        static_for<2 * DC>([&](auto step) __attribute__((always_inline)) {
+          constexpr int st = decltype(step)::value, dc = st >> 1;
+          if constexpr (st + PF < 2 * DC) fa[(st + PF) % (PF + 1)] = afrag(std::integral_constant<int, st + PF>{});
+          if constexpr (st & 1)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
+          else
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], kf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
       const int lo = CAUSAL ? key - q0 : 0;
       const int hi = kok ? seq_len - 1 - q0 : -1;
@@ -626,25 +641,43 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
     __syncthreads();                           // both halves' chunks in LDS
     if (!live) continue;
     // dV^T += dO^T P and dK^T += Q^T dS over the tile's four 16-query chunks,
-    // this wave's 64 coordinates
+    // this wave's 64 coordinates: 16 MFMA steps, the wave's own two chunks
+    // first (chunk kl ^ 2 half for local chunk kl), then the partner's, whose
+    // P and dS are read from LDS at the start; each transposed fragment is
+    // read PF steps ahead of its MFMA
+    {
+      constexpr int PF = 3;
+      bf16x8 xp[2], xds[2];                    // the partner's chunks
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const bool mine = (kc >> 1) == half;
-      const bf16x8 pf = mine ? own_p[kc & 1] : *(const bf16x8*)slot(0, kc);
-      const bf16x8 dsf = mine ? own_ds[kc & 1] : *(const bf16x8*)slot(1, kc);
-      const char* dd = dt + kc * 16 * ROWB;
-      const char* qq = qt + kc * 16 * ROWB;
-#pragma unroll
-      for (int dbl = 0; dbl < DBH; ++dbl) {
-        const bf16x4 dlo = ds_read_tr16(dd + voff[0][dbl]);
-        const bf16x4 dhi = ds_read_tr16(dd + voff[1][dbl]);
-        dvacc[dbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7), pf, dvacc[dbl], 0, 0, 0);
-        const bf16x4 qlo = ds_read_tr16(qq + voff[0][dbl]);
-        const bf16x4 qhi = ds_read_tr16(qq + voff[1][dbl]);
-        dkacc[dbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), dsf, dkacc[dbl], 0, 0, 0);
+      for (int c2 = 0; c2 < 2; ++c2) {
+        xp[c2] = *(const bf16x8*)slot(0, (half ^ 1) * 2 + c2);
+        xds[c2] = *(const bf16x8*)slot(1, (half ^ 1) * 2 + c2);
       }
+      // step t: local chunk t / 4, d block (t / 2) % 2, dV (even) or dK (odd)
+      auto cfrag = [&](auto step) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int t = decltype(step)::value, kl = t >> 2, dbl = (t >> 1) & 1;
+        const int kc = kl ^ (2 * half);
+        const char* base = ((t & 1) ? qt : dt) + kc * 16 * ROWB;
+        const bf16x4 lo = ds_read_tr16(base + voff[0][dbl]);
+        const bf16x4 hi = ds_read_tr16(base + voff[1][dbl]);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 fc[PF + 1];
+      static_for<PF>([&](auto step) __attribute__((always_inline)) {
+        fc[decltype(step)::value] = cfrag(step);
+      });
+      static_for<16>([&](auto step) __attribute__((always_inline)) {
+        constexpr int t = decltype(step)::value, kl = t >> 2, dbl = (t >> 1) & 1;
+        if constexpr (t + PF < 16) fc[(t + PF) % (PF + 1)] = cfrag(std::integral_constant<int, t + PF>{});
+        bf16x8 pb;
+        if constexpr (kl < 2) pb = (t & 1) ? own_ds[kl] : own_p[kl];
+        else pb = (t & 1) ? xds[kl - 2] : xp[kl - 2];
+        if constexpr (t & 1)
+          dkacc[dbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[t % (PF + 1)], pb, dkacc[dbl], 0, 0, 0);
+        else
+          dvacc[dbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[t % (PF + 1)], pb, dvacc[dbl], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
   }
   if (kok) {
