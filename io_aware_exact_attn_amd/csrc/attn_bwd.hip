@@ -222,14 +222,27 @@ bwd_dq_kernel(BwdArgs a) {
     // product into dQ^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // 2 DC MFMA steps, S^T and dP^T alternating, each operand fragment read
+      // PF steps ahead of its MFMA (a scheduling barrier between steps)
+      constexpr int PF = 3;
       f32x16 s, dp;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 kfr = *(const bf16x8*)(kt + kb * 32 * ROWB + koff[dc]);
-        const bf16x8 vfr = *(const bf16x8*)(vt + kb * 32 * ROWB + koff[dc]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, df[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
-      }
+      auto sfrag = [&](auto step) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int st = decltype(step)::value;
+        return *(const bf16x8*)(((st & 1) ? vt : kt) + kb * 32 * ROWB + koff[st >> 1]);
+      };
+      bf16x8 fa[PF + 1];
+      static_for<PF>([&](auto step) __attribute__((always_inline)) {
+        fa[decltype(step)::value] = sfrag(step);
+      });
+      static_for<2 * DC>([&](auto step) __attribute__((always_inline)) {
+        constexpr int st = decltype(step)::value, dc = st >> 1;
+        if constexpr (st + PF < 2 * DC) fa[(st + PF) % (PF + 1)] = sfrag(std::integral_constant<int, st + PF>{});
+        if constexpr (st & 1)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], df[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
+        else
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], qf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
       // P^T and dS^T in place; key of register r: kv0 + kb*32 + (r/4)*8 + hl*4 + r%4.
       // The mask is applied only where some key of the half lies past the
       // wave's first query (causal) or the sequence end.
@@ -245,22 +258,34 @@ bwd_dq_kernel(BwdArgs a) {
       };
       if (dq_half_tile_unmasked(CAUSAL, wq0, kv0 + kb * 32, seq_len)) weights(std::false_type{});
       else weights(std::true_type{});
-      // dQ^T += K^T dS^T, 16 keys at a time
+      // dQ^T += K^T dS^T, 16 keys at a time: 2 DB MFMA steps (chunk t / DB,
+      // d block t % DB), each transposed K fragment read PF2 steps ahead
+      bf16x8 dsf[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         u32x4 w;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(s[8 * c2 + 2 * jj], s[8 * c2 + 2 * jj + 1]);
-        const bf16x8 dsf = __builtin_bit_cast(bf16x8, w);
-        const char* kk = kt + (kb * 2 + c2) * 16 * ROWB;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x4 lo = ds_read_tr16(kk + voff[0][db]);
-          const bf16x4 hi = ds_read_tr16(kk + voff[1][db]);
-          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                              dsf, dqacc[db], 0, 0, 0);
-        }
+        dsf[c2] = __builtin_bit_cast(bf16x8, w);
       }
+      constexpr int PF2 = 2;
+      auto tfrag = [&](auto step) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int t = decltype(step)::value, c2 = t / DB, db = t % DB;
+        const char* kk = kt + (kb * 2 + c2) * 16 * ROWB;
+        const bf16x4 lo = ds_read_tr16(kk + voff[0][db]);
+        const bf16x4 hi = ds_read_tr16(kk + voff[1][db]);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 ft[PF2 + 1];
+      static_for<PF2>([&](auto step) __attribute__((always_inline)) {
+        ft[decltype(step)::value] = tfrag(step);
+      });
+      static_for<2 * DB>([&](auto step) __attribute__((always_inline)) {
+        constexpr int t = decltype(step)::value, c2 = t / DB, db = t % DB;
+        if constexpr (t + PF2 < 2 * DB) ft[(t + PF2) % (PF2 + 1)] = tfrag(std::integral_constant<int, t + PF2>{});
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ft[t % (PF2 + 1)], dsf[c2], dqacc[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
   }
   if (tok) store_row<D>((uint16_t*)a.dq + trow, dqacc, a.scale, hl);
