@@ -488,7 +488,9 @@ bwd_dkdv_kernel(BwdArgs a) {
 // and leaves its two 16-query chunks of P and dS, packed as the next
 // product's B operand, in LDS; after a barrier each wave takes its partner's
 // chunks and accumulates dV^T += dO^T P and dK^T += Q^T dS for all 64 queries
-// but only its own 64 of the 128 coordinates.
+// but only its own 64 of the 128 coordinates.  The dP accumulator starts at
+// D and V is held negated, so the products leave D - dP: dS comes out
+// negated at one multiply per score, and dK is negated where it is stored.
 template <int D, bool CAUSAL, bool PACKED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_pair_kernel(BwdArgs a) {
@@ -525,6 +527,11 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
   bf16x8 kf[DC], vf[DC];
   load_row_frags<D>((const uint16_t*)a.k + krow, rs, kok, hl, kf);
   load_row_frags<D>((const uint16_t*)a.v + krow, rs, kok, hl, vf);
+  // V negated (exactly, by its sign bits): the dP accumulator starts at D and
+  // ends at D - dP, so dS comes out negated and dK is negated at the store
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    vf[dc] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vf[dc]) ^ 0x80008000u);
 
   uint32_t lane_off[CPW];
 #pragma unroll
@@ -606,6 +613,13 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
       // ahead of its MFMA so the LDS latency hides behind earlier MFMAs
       f32x16 s, dp;
       {
+        f32x16 d0;                             // D of each of the 16 query rows
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + half * 32 + g * 8 + hl * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d0[g * 4 + i] = d4[i];
+        }
         constexpr int PF = 3;
         auto afrag = [&](auto step) __attribute__((always_inline)) -> bf16x8 {
           constexpr int st = decltype(step)::value;
@@ -619,7 +633,7 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
           constexpr int st = decltype(step)::value, dc = st >> 1;
           if constexpr (st + PF < 2 * DC) fa[(st + PF) % (PF + 1)] = afrag(std::integral_constant<int, st + PF>{});
           if constexpr (st & 1)
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], vf[dc], dc == 0 ? d0 : dp, 0, 0, 0);
           else
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], kf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
@@ -632,7 +646,6 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
         for (int g = 0; g < 4; ++g) {
           const int qi = half * 32 + g * 8 + hl * 4;
           const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
-          const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = g * 4 + i;
@@ -640,7 +653,7 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
             if constexpr (decltype(masked)::value)
               if (qi + i < lo || qi + i > hi) p = 0.f;
             s[r] = p;
-            dp[r] = p * (dp[r] - d4[i]);
+            dp[r] = p * dp[r];                 // -dS
           }
         }
       };
@@ -713,8 +726,8 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int d = (half * DBH + dbl) * 32 + g * 8 + hl * 4;
         *(u32x2*)((uint16_t*)a.dk + krow + d) =
-            (u32x2){pack_bf16x2(dkacc[dbl][g * 4 + 0] * a.scale, dkacc[dbl][g * 4 + 1] * a.scale),
-                    pack_bf16x2(dkacc[dbl][g * 4 + 2] * a.scale, dkacc[dbl][g * 4 + 3] * a.scale)};
+            (u32x2){pack_bf16x2(dkacc[dbl][g * 4 + 0] * -a.scale, dkacc[dbl][g * 4 + 1] * -a.scale),
+                    pack_bf16x2(dkacc[dbl][g * 4 + 2] * -a.scale, dkacc[dbl][g * 4 + 3] * -a.scale)};
         *(u32x2*)((uint16_t*)a.dv + krow + d) =
             (u32x2){pack_bf16x2(dvacc[dbl][g * 4 + 0], dvacc[dbl][g * 4 + 1]),
                     pack_bf16x2(dvacc[dbl][g * 4 + 2], dvacc[dbl][g * 4 + 3])};
