@@ -151,6 +151,15 @@ bwd_dq_kernel(BwdArgs a) {
   load_row_frags<D>((const uint16_t*)a.dout + trow, rs, tok, hl, df);
   const float lse2 = tok ? a.lse[lrow + t] * kLog2e : 0.f;
   const float dlt = tok ? a.delta[lrow + t] : 0.f;
+  // dO negated (exactly, by its sign bits) and every dP^T sum started at D:
+  // the products leave D - dP, so dS comes out negated and dQ is negated at
+  // the store
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    df[dc] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, df[dc]) ^ 0x80008000u);
+  f32x16 d0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) d0[r] = dlt;
 
   // tile loads
   uint32_t lane_off[CPW];
@@ -238,7 +247,7 @@ bwd_dq_kernel(BwdArgs a) {
         constexpr int st = decltype(step)::value, dc = st >> 1;
         if constexpr (st + PF < 2 * DC) fa[(st + PF) % (PF + 1)] = sfrag(std::integral_constant<int, st + PF>{});
         if constexpr (st & 1)
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], df[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], df[dc], dc == 0 ? d0 : dp, 0, 0, 0);
         else
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st % (PF + 1)], qf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -253,7 +262,7 @@ bwd_dq_kernel(BwdArgs a) {
           float p = fast_exp2(__builtin_fmaf(s[r], a.c, -lse2));
           if constexpr (decltype(masked)::value)
             if ((r >> 2) * 8 + (r & 3) > lim) p = 0.f;
-          s[r] = p * (dp[r] - dlt);
+          s[r] = p * dp[r];                    // -dS^T
         }
       };
       if (dq_half_tile_unmasked(CAUSAL, wq0, kv0 + kb * 32, seq_len)) weights(std::false_type{});
@@ -288,7 +297,7 @@ bwd_dq_kernel(BwdArgs a) {
       });
     }
   }
-  if (tok) store_row<D>((uint16_t*)a.dq + trow, dqacc, a.scale, hl);
+  if (tok) store_row<D>((uint16_t*)a.dq + trow, dqacc, -a.scale, hl);
 }
 
 // ---------------------------------------------------------------------------

@@ -17,13 +17,13 @@ from
     roundings of at most 2^-24 each): this is what is left of dP - D when
     one key holds all the weight and the two nearly cancel, and it moves P
     by a relative |scale| 2^-17 (|q_i| . |k_j| + max_j' |q_i| . |k_j'|);
-    the dK/dV kernel starts its dP sum at D (it accumulates D - dP), which
-    adds |D| <= |dO| . |O| to that sum's absolute terms;
+    the gradient kernels start their dP sums at D (they accumulate D - dP),
+    which adds |D| <= |dO| . |O| to those sums' absolute terms;
   * the bf16 output rounding, half an ulp of the result.
 Propagated without cancellation, element by element:
     |dV~ - dV| <= (2^-7 + e_S) (P^T |dO|)                + half ulp
-    E_c = (2^-7 + e_S) P |dP - D| + P (|D~ - D| + 2^-17 (|dO| |V|^T + c |dO| . |O|)) + 2^-9 |dS|
-    |dQ~ - dQ| <= |scale| E_1 |K|,  |dK~ - dK| <= |scale| E_2^T |Q|  (+ half ulp)
+    E = (2^-7 + e_S) P |dP - D| + P (|D~ - D| + 2^-17 (|dO| |V|^T + 2 |dO| . |O|)) + 2^-9 |dS|
+    |dQ~ - dQ| <= |scale| E |K|,  |dK~ - dK| <= |scale| E^T |Q|  (+ half ulp)
 That is a worst case (all errors of one sign); the Frobenius error of each
 gradient relative to its norm must also stay below 2^-7, which a
 systematic mistake (a dropped mask, a wrong row term) exceeds.
@@ -91,11 +91,11 @@ def _seq_bounds(q, k, v, do, o_gpu, o_ref, scale, causal):
     rel = REL_P + abs(scale) * REL_SUM * (qk + qk.max(axis=1, keepdims=True))
     dov = np.abs(do) @ np.abs(v).T
     doo = (np.abs(do) * np.abs(o_ref)).sum(axis=1, keepdims=True)
-    e0 = rel * p * np.abs(dp - dd) + p * err_d + REL_DS * np.abs(ds)
-    e_q = e0 + p * REL_SUM * (dov + doo)
-    e_k = e0 + p * REL_SUM * (dov + 2 * doo)     # the dP sum that starts at D
-    bq = abs(scale) * (e_q @ np.abs(k))
-    bk = abs(scale) * (e_k.T @ np.abs(q))
+    # the dP sums start at D: |D| <= |dO| . |O| joins their absolute terms,
+    # beside D's own sum
+    e = rel * p * np.abs(dp - dd) + p * (err_d + REL_SUM * (dov + 2 * doo)) + REL_DS * np.abs(ds)
+    bq = abs(scale) * (e @ np.abs(k))
+    bk = abs(scale) * (e.T @ np.abs(q))
     bv = (rel * p).T @ np.abs(do)
     return bq, bk, bv
 
