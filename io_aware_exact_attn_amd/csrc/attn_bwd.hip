@@ -211,19 +211,17 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqacc[db] = (f32x16){};
 
-  if (n_iter > 0) {
-    issue_tile(a.k, 0, 0);
-    issue_tile(a.v, 2, 0);
-  }
-  for (int j = 0; j < n_iter; ++j) {
-    const int P = j & 1;
+  // one key/value tile; the buffer parity is a template constant, so that
+  // every LDS address is a per-lane offset plus an immediate
+  auto tile = [&](auto par, int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                           // tile j landed; tile j - 1 no longer read
     if (j + 1 < n_iter) {
       issue_tile(a.k, P ^ 1, j + 1);
       issue_tile(a.v, 2 + (P ^ 1), j + 1);
     }
-    if (j >= wave_iters) continue;
+    if (j >= wave_iters) return;
     const char* kt = smem + P * TILE;
     const char* vt = smem + (2 + P) * TILE;
     const int kv0 = j * BN;
@@ -296,6 +294,14 @@ bwd_dq_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       });
     }
+  };
+  if (n_iter > 0) {
+    issue_tile(a.k, 0, 0);
+    issue_tile(a.v, 2, 0);
+  }
+  for (int j = 0; j < n_iter; j += 2) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_iter) tile(std::integral_constant<int, 1>{}, j + 1);
   }
   if (tok) store_row<D>((uint16_t*)a.dq + trow, dqacc, -a.scale, hl);
 }
@@ -580,7 +586,7 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
 
   uint32_t qoff[DC];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) qoff[dc] = l32 * ROWB + (((2 * dc + hl) ^ swz<D>(l32)) << 4);
+  for (int dc = 0; dc < DC; ++dc) qoff[dc] = (half * 32 + l32) * ROWB + (((2 * dc + hl) ^ swz<D>(l32)) << 4);
   uint32_t voff[2][DBH];
   {
     const int g16 = lane >> 4;
@@ -605,9 +611,10 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
   for (int dbl = 0; dbl < DBH; ++dbl) dkacc[dbl] = dvacc[dbl] = (f32x16){};
 
-  if (j_begin < j_end) issue_tile(0, j_begin);
-  for (int j = j_begin; j < j_end; ++j) {
-    const int P = (j - j_begin) & 1;
+  // one query tile; the buffer parity is a template constant, so that every
+  // LDS address is a per-lane offset plus an immediate
+  auto tile = [&](auto par, int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                           // tile j landed; last tile's chunks all read
     if (j + 1 < j_end) issue_tile(P ^ 1, j + 1);
@@ -632,7 +639,7 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
         constexpr int PF = 3;
         auto afrag = [&](auto step) __attribute__((always_inline)) -> bf16x8 {
           constexpr int st = decltype(step)::value;
-          return *(const bf16x8*)(((st & 1) ? dt : qt) + half * 32 * ROWB + qoff[st >> 1]);
+          return *(const bf16x8*)(((st & 1) ? dt : qt) + qoff[st >> 1]);
         };
         bf16x8 fa[PF + 1];
         static_for<PF>([&](auto step) __attribute__((always_inline)) {
@@ -686,7 +693,7 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
       }
     }
     __syncthreads();                           // both halves' chunks in LDS
-    if (!live) continue;
+    if (!live) return;
     // dV^T += dO^T P and dK^T += Q^T dS over the tile's four 16-query chunks,
     // this wave's 64 coordinates: 16 MFMA steps, the wave's own two chunks
     // first (chunk kl ^ 2 half for local chunk kl), then the partner's, whose
@@ -726,6 +733,11 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       });
     }
+  };
+  if (j_begin < j_end) issue_tile(0, j_begin);
+  for (int j = j_begin; j < j_end; j += 2) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < j_end) tile(std::integral_constant<int, 1>{}, j + 1);
   }
   if (kok) {
     // this wave's 64 coordinates of the key's dK and dV rows
