@@ -553,7 +553,7 @@ def extra_bwd(args):
            "data": "synthetic (the workload's seeded q, k, v; dO seeded N(0,1) bf16)",
            "config": {"workload": w.name + " backward", "B": B, "H": w.H, "N": N, "d": w.d,
                       "causal": w.causal, "packed": w.varlen, "flop_per_step": F,
-                      "kernels": ["bwd_delta_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]},
+                      "kernels": ["bwd_dq_kernel", "bwd_dkdv_pair_kernel (d = 128) or bwd_dkdv_kernel (d = 64)"]},
            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK["bf16"], "unit": "TFLOP/s",
                         "frac": round(tf / PEAK["bf16"], 4), "traffic": None,
                         "note": "whole step (three launches); per-kernel times from rocprofv3"}}

@@ -187,8 +187,8 @@ ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v,
  *   dq, dk, dv  bf16 outputs, layout of q; fully overwritten.  None of them
  *               may alias an input, delta or each other (other workgroups are
  *               still reading the inputs while a gradient row is written).
- *   d in {64, 128}.  Errors as attn_fwd.  The three kernels are enqueued on
- *   `stream` in order (D, then dQ, then dK and dV).
+ *   d in {64, 128}.  Errors as attn_fwd.  The two kernels are enqueued on
+ *   `stream` in order: dQ (which also writes D), then dK and dV.
  */
 ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, float* delta, void* dq, void* dk, void* dv,

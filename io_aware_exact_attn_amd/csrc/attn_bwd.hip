@@ -12,10 +12,11 @@
 //     dV_j = sum_i P_ij dO_i
 //     dS_ij = P_ij (dO_i . v_j - D_i)
 //     dQ_i = scale sum_j dS_ij k_j,       dK_j = scale sum_i dS_ij q_i.
-// Three kernels, all tile by tile through LDS, nothing N x N in memory:
-//   * delta: D per row, streamed from O and dO;
-//   * dQ: one workgroup per 128 query rows walks the key/value tiles, as the
-//     forward does, with S^T = K Q^T and dP^T = V dO^T and dQ^T += K^T dS^T;
+// Two kernels, both tile by tile through LDS, nothing N x N in memory:
+//   * dQ: one workgroup per 128 query rows first forms D of its rows from
+//     their dO and O (and writes it for the other kernel), then walks the
+//     key/value tiles, as the forward does, with S^T = K Q^T and
+//     dP^T = V dO^T and dQ^T += K^T dS^T;
 //   * dK/dV: one workgroup per 128 keys walks the query tiles, with
 //     S = Q K^T and dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS (at
 //     d = 128 two waves share 32 keys, each forming S and dP for half of a
@@ -45,43 +46,6 @@ constexpr int NW = 4;            // waves per workgroup, 32 rows each
 constexpr int BM = 32 * NW;      // rows (queries or keys) per workgroup
 constexpr int BN = 64;           // rows of a streamed tile
 }  // namespace bwd
-
-// ---------------------------------------------------------------------------
-// D = rowsum(dO * O)
-// ---------------------------------------------------------------------------
-
-template <int D, bool PACKED>
-__global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;                   // lanes per row: one 16-byte granule each
-  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gt / LPR;                // token-head row, (token * H + h)
-  const int g = (int)(gt % LPR);
-  const int64_t rows = (int64_t)(PACKED ? a.N : a.B * a.N) * a.H;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 o = *((const u32x4*)a.o + row * LPR + g);
-    const u32x4 d = *((const u32x4*)a.dout + row * LPR + g);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc = __builtin_fmaf(__uint_as_float(o[w] << 16), __uint_as_float(d[w] << 16), acc);
-      acc = __builtin_fmaf(__uint_as_float(o[w] & 0xffff0000u), __uint_as_float(d[w] & 0xffff0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < rows && g == 0) {
-    const int64_t token = row / a.H;
-    const int h = (int)(row % a.H);
-    int64_t idx;
-    if constexpr (PACKED) {
-      idx = (int64_t)h * a.N + token;
-    } else {
-      const int64_t b = token / a.N, t = token % a.N;
-      idx = (b * a.H + h) * a.N + t;
-    }
-    a.delta[idx] = acc;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // shared pieces of the two gradient kernels
@@ -146,11 +110,26 @@ bwd_dq_kernel(BwdArgs a) {
   const int t = wq0 + l32;
   const bool tok = t < seq_len;
   const int64_t trow = (int64_t)(seq_start + (tok ? t : 0)) * rs + head_off;
-  bf16x8 qf[DC], df[DC];
+  bf16x8 qf[DC], df[DC], of[DC];
   load_row_frags<D>((const uint16_t*)a.q + trow, rs, tok, hl, qf);
   load_row_frags<D>((const uint16_t*)a.dout + trow, rs, tok, hl, df);
+  load_row_frags<D>((const uint16_t*)a.o + trow, rs, tok, hl, of);
   const float lse2 = tok ? a.lse[lrow + t] * kLog2e : 0.f;
-  const float dlt = tok ? a.delta[lrow + t] : 0.f;
+  // D = dO . O of the row, from the fragments: the two halves of the wave
+  // hold the two halves of the row's coordinates and exchange their sums.
+  // D goes to the caller's buffer for the dK/dV kernel, enqueued after this
+  // one.
+  float dlt;
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)df[dc][e], (float)of[dc][e], part);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    dlt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (tok && hl == 0) a.delta[lrow + t] = dlt;
+  }
   // dO negated (exactly, by its sign bits) and every dP^T sum started at D:
   // the products leave D - dP, so dS comes out negated and dQ is negated at
   // the store
@@ -763,14 +742,6 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
 template <int D, bool CAUSAL, bool PACKED>
 static hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
   constexpr int BM = bwd::BM;
-  {
-    const int64_t rows = (int64_t)(PACKED ? a.N : a.B * a.N) * a.H;
-    const int64_t grid = (rows * (D / 8) + 255) / 256;
-    void* args[] = {&a};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_delta_kernel<D, PACKED>),
-                                         dim3((unsigned)grid), dim3(256), args, 0, st);
-    if (e != hipSuccess) return e;
-  }
   if (PACKED) {
     a.slots = (a.N + BM - 1) / BM + a.B;
     a.n_work = a.H * a.slots;
