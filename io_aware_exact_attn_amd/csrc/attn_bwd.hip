@@ -607,13 +607,19 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
       // MFMA steps, S and dP alternating, each operand fragment read PF steps
       // ahead of its MFMA so the LDS latency hides behind earlier MFMAs
       f32x16 s, dp;
+      f32x16 nl;                               // -L log2(e) of the 16 query rows, formed
+                                               // among the MFMAs rather than in the weight loop
       {
         f32x16 d0;                             // D of each of the 16 query rows
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + half * 32 + g * 8 + hl * 4);
+          const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + half * 32 + g * 8 + hl * 4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) d0[g * 4 + i] = d4[i];
+          for (int i = 0; i < 4; ++i) {
+            d0[g * 4 + i] = d4[i];
+            nl[g * 4 + i] = -l4[i] * kLog2e;
+          }
         }
         constexpr int PF = 3;
         auto afrag = [&](auto step) __attribute__((always_inline)) -> bf16x8 {
@@ -640,11 +646,10 @@ bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qi = half * 32 + g * 8 + hl * 4;
-          const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = g * 4 + i;
-            float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
+            float p = fast_exp2(__builtin_fmaf(s[r], a.c, nl[r]));
             if constexpr (decltype(masked)::value)
               if (qi + i < lo || qi + i > hi) p = 0.f;
             s[r] = p;
