@@ -556,7 +556,7 @@ def extra_bwd(args):
                       "kernels": ["bwd_dq_kernel", "bwd_dkdv_pair_kernel (d = 128) or bwd_dkdv_kernel (d = 64)"]},
            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK["bf16"], "unit": "TFLOP/s",
                         "frac": round(tf / PEAK["bf16"], 4), "traffic": None,
-                        "note": "whole step (three launches); per-kernel times from rocprofv3"}}
+                        "note": "whole step (two launches: dQ with D, then dK and dV); per-kernel times from rocprofv3"}}
     if not args.no_cpu_baseline:
         import oracle
         import oracle.backward as ob
