@@ -124,6 +124,13 @@ def _bounds(q, k, v, do, o_gpu, o_ref, scale, causal, cu=None):
 def check_case(bits, scale, causal, cu=None):
     q, k, v, do = bits
     O, dq, dk, dv, delta = run_fwd_bwd(q, k, v, do, scale, causal, cu)
+    return verify_case(bits, O, dq, dk, dv, delta, scale, causal, cu)
+
+
+def verify_case(bits, O, dq, dk, dv, delta, scale, causal, cu=None):
+    """The gradients and D the kernels returned for inputs `bits`, against
+    the oracle under the bounds of this file's docstring."""
+    q, k, v, do = bits
     qf, kf, vf, dof = (oracle.bf16_decode(x) for x in bits)
     Or, _ = oracle_bf16(q, k, v, scale, causal, cu_seqlens=cu)
     want = ob.attention_grads(qf, kf, vf, dof, scale, causal, cu)
@@ -194,6 +201,42 @@ def test_bwd_gradient_outliers():
     q, k, v = (W.normal_bf16(4000 + i, shape, outliers=True) for i in range(3))
     do = W.normal_bf16(4003, shape)
     check_case((q, k, v, do), 1.0 / np.sqrt(128), True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_bwd_max_head_stride(d, causal):
+    """H * d at the boundary's 2^24 limit (H = 2^24 / d heads): a 64-token
+    tile of all heads spans 2^31 bytes, the most the backward kernels' 32-bit
+    tile offsets and buffer sizes allow.  N = 65 gives a full tile and a
+    one-row tail.  Four heads (first, second, middle, last) hold seeded q, k,
+    v and dO, the rest zeros; their gradients and D are checked."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    B, N = 1, 65
+    H = (1 << 24) // d
+    heads = [0, 1, H // 2, H - 1]
+    scale = 1.0 / np.sqrt(d)
+    bits = tuple(W.normal_bf16(9300 + 10 * d + i, (B, N, len(heads), d)) for i in range(4))   # q, k, v, dO
+    dev = []
+    for x in bits:
+        t = torch.zeros((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+        for j, h in enumerate(heads):
+            t[:, :, h] = torch.from_numpy(np.ascontiguousarray(x[:, :, j]).view(np.int16)).view(torch.bfloat16).cuda()
+        dev.append(t)
+    o = torch.full((B, N, H, d), 77.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), 77.0, dtype=torch.float32, device="cuda")
+    ia.attn_fwd(dev[0], dev[1], dev[2], o, lse, B, H, N, d, scale, causal, None, ia.ATTN_BF16)
+    delta = torch.full((B, H, N), 77.0, dtype=torch.float32, device="cuda")
+    g = [torch.full((B, N, H, d), 77.0, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    ia.attn_bwd(dev[0], dev[1], dev[2], o, dev[3], lse, delta, g[0], g[1], g[2], B, H, N, d, scale, causal, None)
+    torch.cuda.synchronize()
+    f = lambda t: t[:, :, heads].float().cpu().numpy().astype(np.float64)
+    O, dq, dk, dv = f(o), f(g[0]), f(g[1]), f(g[2])
+    D = delta[:, heads].cpu().numpy().astype(np.float64)
+    del dev, o, lse, delta, g
+    torch.cuda.empty_cache()
+    verify_case(bits, O, dq, dk, dv, D, scale, bool(causal))
 
 
 @pytest.fixture(scope="module")
