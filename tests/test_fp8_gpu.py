@@ -118,3 +118,40 @@ def test_fp8_deterministic():
     a = run_fp8(q, k, v, qs, ks, vs, 0.1, True)
     b = run_fp8(q, k, v, qs, ks, vs, 0.1, True)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_fp8_max_head_stride(causal):
+    """H * d at the boundary's 2^24 limit (H = 2^17 heads at d = 128): a
+    64-token tile of all heads spans 2^30 bytes of e4m3.  N = 65 gives a full
+    tile and a one-row tail.  Four heads (first, second, middle, last) hold
+    seeded quantised inputs with outliers, the rest zeros under unit scales;
+    those four are compared with the oracle on their dequantised inputs."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    from parity import to_dev
+    B, N, d = 1, 65, 128
+    H = (1 << 24) // d
+    heads = [0, 1, H // 2, H - 1]
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, qs, ks, vs = _quantized(97, (B, N, len(heads), d))
+    dev, sdev = [], []
+    for x, s in ((q, qs), (k, ks), (v, vs)):
+        t = torch.zeros((B, N, H, d), dtype=torch.uint8, device="cuda")
+        st = torch.ones((B, H, s.shape[2]), dtype=torch.float32, device="cuda")
+        for j, h in enumerate(heads):
+            t[:, :, h] = torch.from_numpy(np.ascontiguousarray(x[:, :, j])).cuda()   # the bytes as they are
+            st[:, h] = to_dev(np.ascontiguousarray(s[:, j]))
+        dev.append(t.view(torch.float8_e4m3fn))
+        sdev.append(st)
+    o = torch.full((B, N, H, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ia.attn_fwd_fp8(dev[0], dev[1], dev[2], sdev[0], sdev[1], sdev[2], o, lse, B, H, N, d, scale, causal)
+    torch.cuda.synchronize()
+    O = o[:, :, heads].float().cpu().numpy().astype(np.float64)
+    L = lse[:, heads].cpu().numpy().astype(np.float64)
+    del dev, sdev, o, lse
+    torch.cuda.empty_cache()
+    qd, kd, vd = _deq(q, k, v, qs, ks, vs)
+    Or, Lr = oracle.attention(qd, kd, vd, scale, causal=bool(causal))
+    assert_within(errors(O, Or, L, Lr), TOL_FP8)
