@@ -221,3 +221,65 @@ def test_packed_workload_fp8_sampled():
     print("packed workload fp8", err)
     assert_within(err, TOL_FP8)
     assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+
+
+@pytest.mark.parametrize("kind", ["fp8", "fp8_rotated", "mx_d", "mx_tokens"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_quantizers_max_head_stride(kind, d):
+    """Every quantiser at H * d = 2^24 (the boundary's limit; N = 65: one full
+    128-token block row of 65 tokens, a 32-token MX block and a one-token
+    tail): four seeded heads (first, second, middle, last) bit for bit
+    against the oracle on those heads, and a zero head quantised to zero
+    bytes under the all-zero block's scale."""
+    import torch
+    import io_aware_exact_attn_amd as ia
+    import oracle.mx as omx
+    import oracle.rotation as orot
+    B, N = 1, 65
+    H = (1 << 24) // d
+    heads = [0, 1, H // 2, H - 1]
+    zero_head = 2
+    bits = bf16_input(9500 + d, (B, N, len(heads), d), zero_block=False)
+    x = torch.zeros((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+    for j, h in enumerate(heads):
+        x[:, :, h] = to_dev(np.ascontiguousarray(bits[:, :, j]))
+    y = torch.full((B, N, H, d), 0xAA, dtype=torch.uint8, device="cuda")
+    signs = W.random_signs(9501, d)
+    if kind in ("fp8", "fp8_rotated"):
+        s = torch.full((B, H, 1), SENTINEL, dtype=torch.float32, device="cuda")
+        if kind == "fp8":
+            ia.attn_quantize_fp8(x, y, s, B, H, N, d, None)
+        else:
+            ia.attn_quantize_fp8_rotated(x, y, s, to_dev(signs), B, H, N, d, None)
+    elif kind == "mx_d":
+        s = torch.full((B, N, H, d // 32), 0xAA, dtype=torch.uint8, device="cuda")
+        ia.attn_quantize_mxfp8(x, y, s, B, H, N, d, None, 0)
+    else:
+        s = torch.full((B, H, -(-N // 32), d), 0xAA, dtype=torch.uint8, device="cuda")
+        ia.attn_quantize_mxfp8(x, y, s, B, H, N, d, None, 1)
+    torch.cuda.synchronize()
+    hidx = heads + [zero_head]
+    yh = y[:, :, hidx].cpu().numpy()
+    sh = (s[:, :, hidx] if kind == "mx_d" else s[:, hidx]).cpu().numpy()
+    del x, y, s
+    torch.cuda.empty_cache()
+    xf = oracle.bf16_decode(bits).astype(np.float32)
+    if kind == "fp8":
+        yr, sr = oq.quantize_blocks(xf)
+    elif kind == "fp8_rotated":
+        yr, sr = orot.rotate_quantize_blocks(oracle.bf16_decode(bits), signs)
+    elif kind == "mx_d":
+        yr, sr = omx.quantize_mx_d(oracle.bf16_decode(bits))
+    else:
+        yr, sr = omx.quantize_mx_tokens(oracle.bf16_decode(bits))
+    assert np.array_equal(yh[:, :, :4], yr)
+    if kind.startswith("fp8"):
+        assert np.array_equal(sh[:, :4].view(np.uint32), sr.view(np.uint32))
+        assert np.all(sh[:, 4] == 1.0)                     # an all-zero block's scale
+    elif kind == "mx_d":
+        assert np.array_equal(sh[:, :, :4], sr)
+        assert np.all(sh[:, :, 4] == 127)                  # E8M0 2^0
+    else:
+        assert np.array_equal(sh[:, :4], sr)
+        assert np.all(sh[:, 4] == 127)
+    assert np.all(yh[:, :, 4] == 0)
