@@ -60,6 +60,15 @@ def test_small_shapes_fp8(N, causal):
     assert_within(err, TOL_FP8)
 
 
+
+def test_noncausal_long_rows_fp8():
+    """Non-causal rows over 4096 keys with +-20 outliers in Q, K and V, at
+    the fp8 bound."""
+    q, k, v, qs, ks, vs = _quantized(98, (1, 4096, 2, 128))
+    O, L = run_fp8(q, k, v, qs, ks, vs, 1 / math.sqrt(128), False)
+    Or, Lr = oracle.attention(*_deq(q, k, v, qs, ks, vs), 1 / math.sqrt(128), causal=False)
+    assert_within(errors(O, Or, L, Lr), TOL_FP8)
+
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5])
 def test_scale_values_fp8(scale):
     q, k, v, qs, ks, vs = _quantized(55, (1, 200, 2, 128), outliers="")

@@ -119,6 +119,16 @@ def test_large_scores_qk_outliers(causal, out):
     _check(q, k, v, 1 / math.sqrt(128), causal, out)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_noncausal_long_rows(d):
+    """Non-causal rows over 4096 keys (64 tiles, no mask anywhere but the
+    workgroups' own rows), with the long-context workload's 1 % +-20
+    outliers in Q and K: the lazy reference maximum across many unmasked
+    tiles."""
+    q, k, v = _case(79 + d, (1, 4096, 2, d), outliers="qk")
+    _check(q, k, v, 1 / math.sqrt(d), 0, "bf16")
+
+
 @pytest.mark.parametrize("per_tile,N,d", [(80.0, 300, 128), (170.0, 200, 128), (400.0, 136, 128),
                                            (170.0, 200, 64)])
 @pytest.mark.parametrize("causal", [0, 1])
