@@ -204,6 +204,16 @@ def test_bwd_gradient_outliers():
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_bwd_noncausal_long_rows(d):
+    """Non-causal rows over 4096 keys with +-20 outliers in Q and K: 64 key
+    tiles per dQ workgroup and 64 query tiles per dK/dV workgroup, no mask."""
+    shape = (1, 4096, 2, d)
+    q, k = (W.normal_bf16(4100 + d + i, shape, outliers=True) for i in range(2))
+    v, do = (W.normal_bf16(4102 + d + i, shape) for i in range(2))
+    check_case((q, k, v, do), 1.0 / np.sqrt(d), False)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_bwd_max_head_stride(d, causal):
     """H * d at the boundary's 2^24 limit (H = 2^24 / d heads): a 64-token
