@@ -149,7 +149,7 @@ def test_mxfp8_attention_fixed(N, causal):
     assert_within(errors(O, Or, L, Lr), TOL_FP8)
 
 
-@pytest.mark.parametrize("N", [65, 200, 513, 700, 1000, 2048])
+@pytest.mark.parametrize("N", [65, 200, 513, 700, 1000, 2048, 4096])
 @pytest.mark.parametrize("causal", [False, True])
 def test_mxfp8_attention_all_outliers(N, causal):
     """1% +-20 outliers in all of Q, K and V, at the fp8 bound."""
