@@ -328,6 +328,11 @@ bwd_dkdv_kernel(BwdArgs a) {
   bf16x8 kf[DC], vf[DC];
   load_row_frags<D>((const uint16_t*)a.k + krow, rs, kok, hl, kf);
   load_row_frags<D>((const uint16_t*)a.v + krow, rs, kok, hl, vf);
+  // V negated (exactly, by its sign bits): the dP sums start at D and end at
+  // D - dP, so dS comes out negated and dK is negated at the store
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    vf[dc] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vf[dc]) ^ 0x80008000u);
 
   uint32_t lane_off[CPW];
 #pragma unroll
@@ -388,13 +393,14 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dkacc[db] = dvacc[db] = (f32x16){};
 
-  if (j_begin < j_end) issue_tile(0, j_begin);
-  for (int j = j_begin; j < j_end; ++j) {
-    const int P = (j - j_begin) & 1;
+  // one query tile; the buffer parity is a template constant, so that every
+  // LDS address is a per-lane offset plus an immediate
+  auto tile = [&](auto par, int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 1 < j_end) issue_tile(P ^ 1, j + 1);
-    if (!wave_live || j < wave_begin) continue;
+    if (!wave_live || j < wave_begin) return;
     const char* qt = smem + P * TILE;
     const char* dt = smem + (2 + P) * TILE;
     const int q0 = j * BN;
@@ -406,30 +412,40 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       __builtin_amdgcn_sched_barrier(0);       // one half's loads at a time: fewer live registers
-      f32x16 s, dp;
+      // query of register r: q0 + qb*32 + (r/4)*8 + hl*4 + r%4; its L and D
+      // come from the tile's LDS rows, four at a time: D starts the dP sums,
+      // -L log2(e) is formed beside the MFMAs
+      f32x16 s, dp, d0, nl;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qb * 32 + g * 8 + hl * 4);
+        const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qb * 32 + g * 8 + hl * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          d0[g * 4 + i] = d4[i];
+          nl[g * 4 + i] = -l4[i] * kLog2e;
+        }
+      }
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const bf16x8 qfr = *(const bf16x8*)(qt + qb * 32 * ROWB + qoff[dc]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr, kf[dc], dc == 0 ? (f32x16){} : s, 0, 0, 0);
         const bf16x8 dfr = *(const bf16x8*)(dt + qb * 32 * ROWB + qoff[dc]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? (f32x16){} : dp, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr, vf[dc], dc == 0 ? d0 : dp, 0, 0, 0);
       }
-      // query of register r: q0 + qb*32 + (r/4)*8 + hl*4 + r%4; its L and D
-      // come from the tile's LDS rows, four at a time.  P goes to s, dS to dp.
+      // P goes to s, -dS to dp
       auto weights = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qi = qb * 32 + g * 8 + hl * 4;
-          const f32x4 l4 = *(const f32x4*)(lse_t + P * BN + qi);
-          const f32x4 d4 = *(const f32x4*)(dlt_t + P * BN + qi);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = g * 4 + i;
-            float p = fast_exp2(__builtin_fmaf(s[r], a.c, -l4[i] * kLog2e));
+            float p = fast_exp2(__builtin_fmaf(s[r], a.c, nl[r]));
             if constexpr (decltype(masked)::value)
               if (qi + i < lo || qi + i > hi) p = 0.f;
             s[r] = p;
-            dp[r] = p * (dp[r] - d4[i]);
+            dp[r] = p * dp[r];
           }
         }
       };
@@ -465,9 +481,14 @@ bwd_dkdv_kernel(BwdArgs a) {
         }
       }
     }
+  };
+  if (j_begin < j_end) issue_tile(0, j_begin);
+  for (int j = j_begin; j < j_end; j += 2) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < j_end) tile(std::integral_constant<int, 1>{}, j + 1);
   }
   if (kok) {
-    store_row<D>((uint16_t*)a.dk + krow, dkacc, a.scale, hl);
+    store_row<D>((uint16_t*)a.dk + krow, dkacc, -a.scale, hl);
     store_row<D>((uint16_t*)a.dv + krow, dvacc, 1.f, hl);
   }
 }
